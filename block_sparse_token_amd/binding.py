@@ -1,0 +1,189 @@
+"""ctypes binding of libuniprefill.so (include/uniprefill.h).
+
+Argument marshalling only: every function passes torch tensors' device
+pointers and the current HIP stream to the C entry point of the same name and
+raises ``UniprefillError`` with the library's message on a non-OK status.
+torch is imported first so the library binds to the HIP runtime torch has
+already loaded (both carry the soname libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libuniprefill.so")
+
+UP_F32, UP_BF16 = 0, 1
+_DT = {torch.float32: UP_F32, torch.bfloat16: UP_BF16}
+
+c_i32, c_size, c_vp, c_f32, c_f64 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
+
+
+class UniprefillError(RuntimeError):
+    pass
+
+
+class UpBatch(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", c_i32),
+        ("num_tokens", c_i32),
+        ("cu_seqlens", c_vp),
+        ("ctx_lens", c_vp),
+        ("positions", c_vp),
+        ("slot_mapping", c_vp),
+        ("block_table", c_vp),
+        ("max_pages", c_i32),
+        ("page_size", c_i32),
+    ]
+
+
+class UpRows(ctypes.Structure):
+    _fields_ = [("src", c_vp), ("dst", c_vp), ("row_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise UniprefillError(
+                f"{LIB_PATH} is missing; build it with `python -m block_sparse_token_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        bp = ctypes.POINTER(UpBatch)
+        sig = {
+            "up_last_error": (ctypes.c_char_p, []),
+            "up_version": (ctypes.c_char_p, []),
+            "up_block_offsets": (c_i32, [bp, c_i32, c_vp, c_vp]),
+            "up_attn_workspace_bytes": (c_size, [bp, c_i32, c_i32, c_i32, c_i32]),
+            "up_prefill_attn": (c_i32, [bp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_f32, c_i32, c_f32, c_vp, c_i32, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_size, c_vp]),
+            "up_block_scores": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+            "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
+            "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
+            "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                   ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
+            "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
+            "up_compact"]
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        msg = lib().up_last_error().decode()
+        raise UniprefillError(f"{what} failed (status {st}): {msg}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if t.device.type != "cuda":
+        raise UniprefillError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise UniprefillError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Batch:
+    """Device metadata of one packed batch (see ``up_batch`` in the header)."""
+
+    def __init__(self, cu_seqlens, ctx_lens, positions, slot_mapping, block_table=None,
+                 num_tokens=None, page_size=16):
+        self.cu_seqlens = cu_seqlens
+        self.ctx_lens = ctx_lens
+        self.positions = positions
+        self.slot_mapping = slot_mapping
+        self.block_table = block_table
+        self.num_seqs = int(cu_seqlens.numel() - 1)
+        self.num_tokens = int(num_tokens if num_tokens is not None else positions.numel())
+        self.page_size = page_size
+        self.max_pages = int(block_table.shape[1]) if block_table is not None else 0
+        self._s = UpBatch(self.num_seqs, self.num_tokens, _p(cu_seqlens).value,
+                          _p(ctx_lens).value if ctx_lens is not None else None,
+                          _p(positions).value if positions is not None else None,
+                          _p(slot_mapping).value if slot_mapping is not None else None,
+                          _p(block_table).value if block_table is not None else None,
+                          self.max_pages, page_size)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def up_version() -> str:
+    return lib().up_version().decode()
+
+
+def up_block_offsets(batch: Batch, block_size: int, cu_blocks, stream=None):
+    _check(lib().up_block_offsets(batch.ref, block_size, _p(cu_blocks), _stream(stream)),
+           "up_block_offsets")
+
+
+def up_attn_workspace_bytes(batch: Batch, dtype, Hq, Hkv, D) -> int:
+    return int(lib().up_attn_workspace_bytes(batch.ref, _DT[dtype], Hq, Hkv, D))
+
+
+def up_prefill_attn(batch: Batch, q, k, v, k_cache, v_cache, out, workspace, *, rope_theta=0.0,
+                    window=0, sm_scale=0.0, score_flags=None, block_size=0, cu_blocks=None,
+                    block_mass=None, lse=None, stream=None):
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, k_cache, v_cache, out)):
+        raise UniprefillError("q, k, v, caches and out must share one dtype (float32 or bfloat16)")
+    _check(lib().up_prefill_attn(batch.ref, _DT[q.dtype], Hq, Hkv, D, _p(q), _p(k), _p(v),
+                                 _p(k_cache), _p(v_cache), float(rope_theta), int(window),
+                                 float(sm_scale), _p(score_flags), int(block_size), _p(cu_blocks),
+                                 _p(block_mass), _p(out), _p(lse), _p(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "up_prefill_attn")
+
+
+def up_block_scores(batch: Batch, Hq, block_size, cu_blocks, score_flags, block_mass, scores,
+                    stream=None):
+    _check(lib().up_block_scores(batch.ref, Hq, block_size, _p(cu_blocks), _p(score_flags),
+                                 _p(block_mass), _p(scores), _stream(stream)), "up_block_scores")
+
+
+def up_topp_select(batch: Batch, block_size, cu_blocks, score_flags, p, scores, keep,
+                   kept_blocks=None, stream=None):
+    _check(lib().up_topp_select(batch.ref, block_size, _p(cu_blocks), _p(score_flags), float(p),
+                                _p(scores), _p(keep), _p(kept_blocks), _stream(stream)),
+           "up_topp_select")
+
+
+def up_compact_workspace_bytes(num_seqs, num_blocks) -> int:
+    return int(lib().up_compact_workspace_bytes(num_seqs, num_blocks))
+
+
+def up_compact(batch: Batch, block_size, cu_blocks, keep, num_blocks, rows, index_map,
+               cu_seqlens_out, num_kept, workspace, stream=None):
+    """``rows``: list of (src, dst) tensors whose first dimension is the token."""
+    arr = (UpRows * max(1, len(rows)))()
+    for i, (src, dst) in enumerate(rows):
+        rb = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
+        arr[i] = UpRows(_p(src).value, _p(dst).value, rb)
+    _check(lib().up_compact(batch.ref, block_size, _p(cu_blocks), _p(keep), int(num_blocks),
+                            len(rows), arr, _p(index_map), _p(cu_seqlens_out), _p(num_kept),
+                            _p(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream)), "up_compact")

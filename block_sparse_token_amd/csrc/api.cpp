@@ -1,0 +1,261 @@
+// Host side of the C ABI declared in include/uniprefill.h: argument
+// validation, workspace carving and kernel launches.  No allocation, no
+// synchronisation, no device state.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/uniprefill.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+up_status fail(up_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+up_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return UP_OK;
+  return fail(UP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_block_size(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+
+up_status check_batch(const up_batch* b, bool need_positions) {
+  if (!b) return fail(UP_ERR_INVALID, "batch is NULL");
+  if (b->num_seqs <= 0) return fail(UP_ERR_INVALID, "num_seqs must be >= 1 (got %d)", b->num_seqs);
+  if (b->num_tokens < b->num_seqs)
+    return fail(UP_ERR_INVALID, "num_tokens (%d) < num_seqs (%d)", b->num_tokens, b->num_seqs);
+  if (!b->cu_seqlens) return fail(UP_ERR_INVALID, "cu_seqlens is NULL");
+  if (need_positions) {
+    if (!b->ctx_lens) return fail(UP_ERR_INVALID, "ctx_lens is NULL");
+    if (!b->positions) return fail(UP_ERR_INVALID, "positions is NULL");
+    if (!b->slot_mapping) return fail(UP_ERR_INVALID, "slot_mapping is NULL");
+    if (b->page_size != up::kPageSize)
+      return fail(UP_ERR_UNSUPPORTED, "page_size must be %d (got %d)", up::kPageSize,
+                  b->page_size);
+    if (b->block_table && b->max_pages <= 0)
+      return fail(UP_ERR_INVALID, "max_pages must be >= 1 with a block table");
+  }
+  return UP_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int positions_per_tile(up_dtype dt, int D, int G) {
+  return dt == UP_BF16 ? up::attn_bf16_positions_per_tile(D, G)
+                       : up::attn_f32_positions_per_tile(D, G);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* up_last_error(void) { return g_err.c_str(); }
+
+const char* up_version(void) { return "uniprefill 0.1 gfx950"; }
+
+up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
+                           void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+  if (!cu_blocks) return fail(UP_ERR_INVALID, "cu_blocks is NULL");
+  return device_status(up::launch_block_offsets(batch->cu_seqlens, batch->num_seqs, block_size,
+                                                cu_blocks, as_stream(stream)),
+                       "block offsets launch");
+}
+
+size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                               int32_t D) {
+  if (!batch || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 0;
+  const int G = Hq / Hkv;
+  if (G > 32) return 0;
+  const int P = positions_per_tile(dtype, D, G);
+  if (P <= 0) return 0;
+  return 16 + sizeof(int2) * up::work_capacity(batch->num_tokens, batch->num_seqs, P);
+}
+
+up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                          int32_t D, const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, float rope_theta, int32_t window, float sm_scale,
+                          const uint8_t* score_flags, int32_t block_size,
+                          const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  up_status st = check_batch(batch, true);
+  if (st) return st;
+  if (dtype != UP_F32 && dtype != UP_BF16) return fail(UP_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G > 32 || (G & (G - 1)))
+    return fail(UP_ERR_UNSUPPORTED, "Hq / Hkv must be a power of two <= 32 (got %d)", G);
+  if (D != 64 && D != 128) return fail(UP_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", D);
+  if (!q || !k || !v || !k_cache || !v_cache || !out)
+    return fail(UP_ERR_INVALID, "q, k, v, k_cache, v_cache and out must be non-NULL");
+  if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace) & 15) return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (!(rope_theta == rope_theta) || !(sm_scale == sm_scale))
+    return fail(UP_ERR_INVALID, "rope_theta and sm_scale must not be NaN");
+  if (score_flags) {
+    if (!valid_block_size(block_size))
+      return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    if (!cu_blocks || !block_mass)
+      return fail(UP_ERR_INVALID, "scoring needs cu_blocks and block_mass");
+  }
+  if (batch->num_seqs > up::kMaxSeqsPlan)
+    return fail(UP_ERR_UNSUPPORTED, "at most %d segments per call (got %d)", up::kMaxSeqsPlan,
+                batch->num_seqs);
+  const size_t need = up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D);
+  if (workspace_bytes < need)
+    return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  hipStream_t s = as_stream(stream);
+  const bool bf16 = dtype == UP_BF16;
+  const int P = positions_per_tile(dtype, D, G);
+  const int cap = (int)up::work_capacity(batch->num_tokens, batch->num_seqs, P);
+
+  // rotary frequencies in turns per position: theta^(-2j/D) / (2 pi)
+  double rev[up::kMaxRopePairs] = {0};
+  const int rope = rope_theta > 0.f;
+  if (rope)
+    for (int j = 0; j < D / 2; ++j)
+      rev[j] = pow((double)rope_theta, -2.0 * j / D) / (2.0 * 3.141592653589793238462643383279502884);
+
+  up::RopeArgs ra;
+  ra.k = k;
+  ra.v = v;
+  ra.k_cache = k_cache;
+  ra.v_cache = v_cache;
+  ra.cu_seqlens = batch->cu_seqlens;
+  ra.positions = batch->positions;
+  ra.slot_mapping = batch->slot_mapping;
+  ra.S = batch->num_seqs;
+  ra.T = batch->num_tokens;
+  ra.Hkv = Hkv;
+  ra.rope = rope;
+  for (int j = 0; j < up::kMaxRopePairs; ++j) ra.rope_rev[j] = rev[j];
+  hipError_t e = up::launch_rope_kv(ra, bf16, D, s);
+  if (e != hipSuccess) return device_status(e, "rope/kv-write launch");
+
+  int32_t* count = (int32_t*)workspace;
+  int2* items = (int2*)((char*)workspace + 16);
+  e = up::launch_plan(batch->cu_seqlens, batch->ctx_lens, score_flags, batch->num_seqs, P, window,
+                      items, count, cap, s);
+  if (e != hipSuccess) return device_status(e, "work-plan launch");
+
+  up::AttnArgs a;
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cu_seqlens = batch->cu_seqlens;
+  a.ctx_lens = batch->ctx_lens;
+  a.positions = batch->positions;
+  a.slot_mapping = batch->slot_mapping;
+  a.block_table = batch->block_table;
+  a.score_flags = score_flags;
+  a.cu_blocks = cu_blocks;
+  a.block_mass = block_mass;
+  a.items = items;
+  a.item_count = count;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.max_pages = batch->max_pages;
+  a.block_size = block_size;
+  a.window = window > 0 ? window : 0;
+  a.rope = rope;
+  a.scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
+  a.scale_log2 = (float)((double)a.scale * 1.4426950408889634073599246810018921);
+  for (int j = 0; j < up::kMaxRopePairs; ++j) a.rope_rev[j] = rev[j];
+  e = bf16 ? up::launch_attn_bf16(a, D, cap, s) : up::launch_attn_f32(a, D, cap, s);
+  return device_status(e, "attention launch");
+}
+
+up_status up_block_scores(const up_batch* batch, int32_t Hq, int32_t block_size,
+                          const int32_t* cu_blocks, const uint8_t* score_flags,
+                          const float* block_mass, float* scores, void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  if (Hq <= 0) return fail(UP_ERR_INVALID, "Hq must be >= 1");
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+  if (!cu_blocks || !scores) return fail(UP_ERR_INVALID, "cu_blocks and scores must be non-NULL");
+  if (score_flags && !block_mass) return fail(UP_ERR_INVALID, "block_mass is NULL");
+  return device_status(up::launch_block_scores(batch->cu_seqlens, cu_blocks, score_flags,
+                                               block_mass, scores, batch->num_seqs, Hq,
+                                               as_stream(stream)),
+                       "block scores launch");
+}
+
+up_status up_topp_select(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                         const uint8_t* score_flags, double p, const float* scores,
+                         uint8_t* keep, int32_t* kept_blocks, void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+  if (!(p >= 0.0 && p <= 1.0)) return fail(UP_ERR_INVALID, "p must be in [0, 1] (got %g)", p);
+  if (!cu_blocks || !keep) return fail(UP_ERR_INVALID, "cu_blocks and keep must be non-NULL");
+  if (score_flags && !scores) return fail(UP_ERR_INVALID, "scores is NULL");
+  const uint32_t p_fx = (uint32_t)floor(ldexp(p, 22) + 0.5);
+  const int keep_all = p >= 1.0;
+  return device_status(up::launch_topp(cu_blocks, score_flags, scores, keep, kept_blocks,
+                                       batch->num_seqs, p_fx, keep_all, as_stream(stream)),
+                       "top-p launch");
+}
+
+size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks) {
+  (void)num_seqs;
+  if (num_blocks <= 0) return 0;
+  return 2 * sizeof(int32_t) * ((size_t)num_blocks + 4);
+}
+
+up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                     const uint8_t* keep, int32_t num_blocks, int32_t n_rows,
+                     const up_rows* rows, int32_t* index_map, int32_t* cu_seqlens_out,
+                     int32_t* num_kept, void* workspace, size_t workspace_bytes, void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+  if (!cu_blocks || !keep || !index_map || !cu_seqlens_out || !num_kept)
+    return fail(UP_ERR_INVALID, "cu_blocks, keep, index_map, cu_seqlens_out, num_kept must be non-NULL");
+  if (num_blocks < batch->num_seqs)
+    return fail(UP_ERR_INVALID, "num_blocks (%d) < num_seqs (%d)", num_blocks, batch->num_seqs);
+  if (n_rows < 0 || n_rows > up::kMaxRowTensors)
+    return fail(UP_ERR_UNSUPPORTED, "n_rows must be in [0, %d] (got %d)", up::kMaxRowTensors, n_rows);
+  if (n_rows && !rows) return fail(UP_ERR_INVALID, "rows is NULL");
+  up::RowCopy rc[up::kMaxRowTensors];
+  for (int i = 0; i < n_rows; ++i) {
+    if (!rows[i].src || !rows[i].dst || rows[i].row_bytes <= 0)
+      return fail(UP_ERR_INVALID, "rows[%d]: src/dst NULL or row_bytes <= 0", i);
+    rc[i].src = (const uint8_t*)rows[i].src;
+    rc[i].dst = (uint8_t*)rows[i].dst;
+    rc[i].row_bytes = rows[i].row_bytes;
+  }
+  if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
+  const size_t need = up_compact_workspace_bytes(batch->num_seqs, num_blocks);
+  if (workspace_bytes < need)
+    return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  int32_t* block_out = (int32_t*)workspace;
+  int32_t* block_seg = block_out + num_blocks + 4;
+  return device_status(up::launch_compact(batch->cu_seqlens, cu_blocks, keep, batch->num_seqs,
+                                          num_blocks, block_size, rc, n_rows, index_map,
+                                          cu_seqlens_out, num_kept, block_out, block_seg,
+                                          as_stream(stream)),
+                       "compaction launch");
+}
+
+}  // extern "C"

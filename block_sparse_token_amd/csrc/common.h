@@ -1,0 +1,94 @@
+// Internal declarations shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+namespace up {
+
+// ---------------------------------------------------------------- limits
+constexpr int kPageSize = 16;
+constexpr int kMaxSeqsPlan = 8192;  // segments per call the work planner handles
+constexpr int kMaxRopePairs = 64;   // D / 2 for D = 128
+
+// ---------------------------------------------------------------- work items
+// One attention work item = (segment, query tile) or a score item for a
+// flagged segment (tile == kScoreTile).  Launched once per KV head.
+constexpr int kScoreTile = -1;
+
+// Work list layout inside the attention workspace (bytes):
+//   [0, 16): int32 item count
+//   [16, ...): int2 items[capacity]
+inline size_t work_capacity(int T, int S, int positions_per_tile) {
+  return (size_t)((T + positions_per_tile - 1) / positions_per_tile) + 2 * (size_t)S + 1;
+}
+
+// ---------------------------------------------------------------- kernel parameters
+struct AttnArgs {
+  const void* q;
+  void* out;
+  float* lse;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_seqlens;
+  const int32_t* ctx_lens;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  const int32_t* block_table;
+  const uint8_t* score_flags;
+  const int32_t* cu_blocks;
+  float* block_mass;
+  const int2* items;
+  const int32_t* item_count;
+  int Hq, Hkv, G, max_pages, block_size, window, rope;
+  float scale;       // logit scale (1/sqrt(D) by default)
+  float scale_log2;  // scale * log2(e)
+  // rotary frequencies: rev[j] = theta^(-2j/D) / (2 pi) (turns per position)
+  double rope_rev[kMaxRopePairs];
+};
+
+struct RopeArgs {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* cu_seqlens;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  int S, T, Hkv, rope;
+  double rope_rev[kMaxRopePairs];
+};
+
+// ---------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error.
+hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,
+                                int32_t* cu_blocks, hipStream_t st);
+hipError_t launch_plan(const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                       const uint8_t* score_flags, int S, int positions_per_tile, int window,
+                       int2* items, int32_t* count, int capacity, hipStream_t st);
+hipError_t launch_rope_kv(const RopeArgs& a, bool bf16, int D, hipStream_t st);
+int attn_bf16_positions_per_tile(int D, int G);
+hipError_t launch_attn_bf16(const AttnArgs& a, int D, int capacity, hipStream_t st);
+int attn_f32_positions_per_tile(int D, int G);
+hipError_t launch_attn_f32(const AttnArgs& a, int D, int capacity, hipStream_t st);
+hipError_t launch_block_scores(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                               const uint8_t* flags, const float* mass, float* scores, int S,
+                               int Hq, hipStream_t st);
+hipError_t launch_topp(const int32_t* cu_blocks, const uint8_t* flags, const float* scores,
+                       uint8_t* keep, int32_t* kept_blocks, int S, uint32_t p_fx, int keep_all,
+                       hipStream_t st);
+struct RowCopy {
+  const uint8_t* src;
+  uint8_t* dst;
+  int64_t row_bytes;
+};
+constexpr int kMaxRowTensors = 16;
+hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                          const uint8_t* keep, int S, int num_blocks, int block_size,
+                          const RowCopy* rows, int n_rows, int32_t* index_map,
+                          int32_t* cu_seqlens_out, int32_t* num_kept, int32_t* block_out,
+                          int32_t* block_seg, hipStream_t st);
+
+}  // namespace up

@@ -1,0 +1,163 @@
+// Compaction of the kept tokens (UniPrefill review, "Method & Key Results":
+// the removed tokens take no part in any later sublayer, so later layers see
+// only the kept rows).
+//
+// Pass 1 (one workgroup): exclusive scan over blocks of (kept ? length : 0)
+// gives each kept block's first output row, the per-segment output offsets
+// (cu_seqlens_out) and the kept count.  Pass 2: the rows of one block are
+// contiguous in the input and in the output, so each kept block is a
+// contiguous byte range per row tensor; workgroups copy slices of those
+// ranges with 16-byte vector loads and stores and write the index map.
+#include "common.h"
+
+namespace up {
+
+__global__ __launch_bounds__(1024) void compact_scan_kernel(
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
+    const uint8_t* __restrict__ keep, int S, int B, int32_t* __restrict__ block_out,
+    int32_t* __restrict__ block_seg, int32_t* __restrict__ cu_out, int32_t* __restrict__ num_kept) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int NB = cu_blocks[S];
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < NB; base += 1024) {
+    const int k = base + tid;
+    int v = 0, s = 0;
+    if (k < NB) {
+      int lo = 0, hi = S - 1;  // segment with cu_blocks[s] <= k < cu_blocks[s+1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu_blocks[mid] <= k) lo = mid; else hi = mid - 1;
+      }
+      s = lo;
+      const int n = cu_seqlens[s + 1] - cu_seqlens[s];
+      const int i0 = (k - cu_blocks[s]) * B;
+      v = keep[k] ? min(B, n - i0) : 0;
+      block_seg[k] = s;
+    }
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wid] = x;
+    __syncthreads();
+    int off = carry;
+    for (int w = 0; w < wid; ++w) off += wsum[w];
+    const int excl = off + x - v;
+    if (k < NB) {
+      block_out[k] = excl;
+      if (k == cu_blocks[s]) cu_out[s] = excl;
+    }
+    __syncthreads();
+    if (tid == 1023) carry = off + x;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    cu_out[S] = carry;
+    *num_kept = carry;
+  }
+}
+
+struct GatherArgs {
+  const int32_t* cu_seqlens;
+  const int32_t* cu_blocks;
+  const uint8_t* keep;
+  const int32_t* block_out;
+  const int32_t* block_seg;
+  int32_t* index_map;
+  int S, B, n_rows;
+  RowCopy rows[kMaxRowTensors];
+};
+
+__device__ inline void copy_range(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                  long nbytes, int part, int nparts) {
+  const int tid = threadIdx.x;
+  const bool vec = ((((uintptr_t)src) | ((uintptr_t)dst) | (uintptr_t)nbytes) & 15) == 0;
+  if (vec) {
+    const long n16 = nbytes >> 4;
+    const long per = (n16 + nparts - 1) / nparts;
+    const long a = part * per, b = min(n16, a + per);
+    const uint4* s4 = (const uint4*)src;
+    uint4* d4 = (uint4*)dst;
+    long i = a + tid;
+    for (; i + 3 * 256 < b; i += 4 * 256) {
+      const uint4 x0 = s4[i], x1 = s4[i + 256], x2 = s4[i + 512], x3 = s4[i + 768];
+      d4[i] = x0;
+      d4[i + 256] = x1;
+      d4[i + 512] = x2;
+      d4[i + 768] = x3;
+    }
+    for (; i < b; i += 256) d4[i] = s4[i];
+  } else if (((((uintptr_t)src) | ((uintptr_t)dst) | (uintptr_t)nbytes) & 3) == 0) {
+    const long n4 = nbytes >> 2;
+    const long per = (n4 + nparts - 1) / nparts;
+    const long a = part * per, b = min(n4, a + per);
+    const uint32_t* s4 = (const uint32_t*)src;
+    uint32_t* d4 = (uint32_t*)dst;
+    for (long i = a + tid; i < b; i += 256) d4[i] = s4[i];
+  } else {
+    const long per = (nbytes + nparts - 1) / nparts;
+    const long a = part * per, b = min(nbytes, a + per);
+    for (long i = a + tid; i < b; i += 256) dst[i] = src[i];
+  }
+}
+
+__global__ __launch_bounds__(256) void compact_gather_kernel(GatherArgs g) {
+  const int k = blockIdx.x;
+  const int NB = g.cu_blocks[g.S];
+  if (k >= NB || !g.keep[k]) return;
+  const int s = g.block_seg[k];
+  const int n = g.cu_seqlens[s + 1] - g.cu_seqlens[s];
+  const int i0 = (k - g.cu_blocks[s]) * g.B;
+  const int len = min(g.B, n - i0);
+  const int src_row = g.cu_seqlens[s] + i0;
+  const int dst_row = g.block_out[k];
+  const int part = blockIdx.y, nparts = gridDim.y;
+  if (part == 0)
+    for (int r = threadIdx.x; r < len; r += 256) g.index_map[dst_row + r] = src_row + r;
+  for (int t = 0; t < g.n_rows; ++t) {
+    const long rb = g.rows[t].row_bytes;
+    copy_range(g.rows[t].src + (long)src_row * rb, g.rows[t].dst + (long)dst_row * rb, len * rb,
+               part, nparts);
+  }
+}
+
+hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                          const uint8_t* keep, int S, int num_blocks, int block_size,
+                          const RowCopy* rows, int n_rows, int32_t* index_map,
+                          int32_t* cu_seqlens_out, int32_t* num_kept, int32_t* block_out,
+                          int32_t* block_seg, hipStream_t st) {
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, cu_blocks, keep,
+                     S, block_size, block_out, block_seg, cu_seqlens_out, num_kept);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GatherArgs g;
+  g.cu_seqlens = cu_seqlens;
+  g.cu_blocks = cu_blocks;
+  g.keep = keep;
+  g.block_out = block_out;
+  g.block_seg = block_seg;
+  g.index_map = index_map;
+  g.S = S;
+  g.B = block_size;
+  g.n_rows = n_rows;
+  long max_block_bytes = 0;
+  for (int i = 0; i < n_rows; ++i) {
+    g.rows[i] = rows[i];
+    max_block_bytes = max_block_bytes > rows[i].row_bytes * block_size
+                          ? max_block_bytes
+                          : rows[i].row_bytes * block_size;
+  }
+  // split each block's copy into ~64 KiB slices
+  int parts = (int)((max_block_bytes + 65535) / 65536);
+  if (parts < 1) parts = 1;
+  if (parts > 64) parts = 64;
+  hipLaunchKernelGGL(compact_gather_kernel, dim3(num_blocks, parts), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace up

@@ -1,0 +1,216 @@
+/*
+ * uniprefill.h - C ABI of the packed, chunked prefill operator for MI355X
+ * (gfx950): causal attention over a continuously batched packed prefill with
+ * fused block-importance mass, block scores, top-p block selection and
+ * compaction of the kept tokens.
+ *
+ * Sources of the operations (web pages; no code exists on them):
+ *  - UniPrefill paper entry (chatpaper), abstract: a token-level prefill
+ *    accelerator packaged as a continuous-batching operator.
+ *  - UniPrefill review, "Key Terms & Definitions" (Top-p Token Selection) and
+ *    "Method & Key Results": the input is split into token blocks, an
+ *    importance per block is estimated at a full-attention layer, the fewest
+ *    blocks whose cumulative importance reaches p are kept, and the dropped
+ *    tokens skip all later sublayers.
+ *  - Ultralytics glossary "Chunked Prefill", "How chunked prefill works": a
+ *    chunk attends the cached keys/values of all earlier chunks plus its own
+ *    tokens under a causal mask over absolute positions; "Related serving
+ *    techniques": the KV cache lives in fixed-size pages.
+ *  - Prepacking summary, "Technical framework" / "Key design": prompts are
+ *    concatenated into one sequence with a block-diagonal attention mask and
+ *    per-prompt positions.
+ *
+ * The pages give no importance formula.  This library's definition: the
+ * importance of key block b of a segment is the softmax probability mass
+ * that the rows of the segment's last query block put on b, summed over all
+ * query heads and those rows, normalised over the segment's blocks; the
+ * first and last blocks are always kept and count toward p.
+ *
+ * Conventions for every call
+ *  - All pointers are device pointers unless marked (host).
+ *  - The caller allocates everything: inputs, outputs (sized to the
+ *    capacities named below), KV caches and workspaces.  The library
+ *    allocates and frees no memory and keeps no device state.
+ *  - Every call is asynchronous on ``stream`` (a hipStream_t; NULL = the
+ *    null stream) and never synchronises.
+ *  - Arguments are validated on the host before any launch; on failure the
+ *    call returns a negative status, launches nothing, writes no output and
+ *    sets the text returned by up_last_error() for the calling thread.  A
+ *    failed launch returns UP_ERR_DEVICE.
+ *  - Device-side preconditions are the caller's: cu_seqlens non-decreasing
+ *    with every segment holding >= 1 token, cu_seqlens[S] <= T, positions
+ *    strictly increasing inside a segment and >= that segment's ctx_len,
+ *    page ids in [0, num_pages), slots in range, cu_blocks consistent with
+ *    cu_seqlens and block_size.
+ *  - The library is thread-safe; its only global state is the thread-local
+ *    error text.
+ */
+#ifndef UNIPREFILL_H
+#define UNIPREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int up_status;
+#define UP_OK 0
+#define UP_ERR_INVALID (-1)     /* bad argument (null pointer, size, range)      */
+#define UP_ERR_UNSUPPORTED (-2) /* valid but not built (head dim, block size...) */
+#define UP_ERR_WORKSPACE (-3)   /* workspace smaller than the size query says    */
+#define UP_ERR_DEVICE (-4)      /* a HIP launch failed; text has hipGetErrorString */
+
+typedef enum { UP_F32 = 0, UP_BF16 = 1 } up_dtype;
+
+/* Text describing the last non-OK status returned on this thread. */
+const char* up_last_error(void);
+/* Library version string, e.g. "uniprefill 0.1 gfx950". */
+const char* up_version(void);
+
+/*
+ * One packed batch (one engine step).  Segment s owns packed rows
+ * [cu_seqlens[s], cu_seqlens[s+1]); it continues a prompt that already has
+ * ctx_lens[s] tokens in the paged KV cache (0 for a fresh prompt).  Cached
+ * token i of segment s has position i and lives at page
+ * block_table[s * max_pages + i / page_size], offset i % page_size.  The
+ * segment's own token t has position positions[t] and its K/V go to slot
+ * slot_mapping[t] = page * page_size + offset.
+ */
+typedef struct up_batch {
+  int32_t num_seqs;             /* (host) S >= 1                                        */
+  int32_t num_tokens;           /* (host) T: row capacity of the packed arrays; the
+                                   tokens in use are cu_seqlens[S] <= T (device value)   */
+  const int32_t* cu_seqlens;    /* [S+1], cu_seqlens[0] = 0                              */
+  const int32_t* ctx_lens;      /* [S] cached tokens before each segment                */
+  const int32_t* positions;     /* [T] per-prompt positions (gapped after compaction)   */
+  const int32_t* slot_mapping;  /* [T] KV slot of each token, >= 0                       */
+  const int32_t* block_table;   /* [S, max_pages] page ids; may be NULL if every
+                                   ctx_len is 0                                          */
+  int32_t max_pages;            /* (host) row length of block_table                      */
+  int32_t page_size;            /* (host) tokens per page; must be 16                    */
+} up_batch;
+
+/*
+ * Block offsets: cu_blocks[s+1] - cu_blocks[s] = ceil(n_s / block_size),
+ * cu_blocks[0] = 0, blocks counted from each segment's start (the last one
+ * may be short).  cu_blocks: [S+1] int32 output.
+ * block_size: 16, 32, 64 or 128.
+ */
+up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
+                           void* stream);
+
+/*
+ * Workspace bytes up_prefill_attn needs for this batch shape (the work list
+ * of query tiles and score items).
+ */
+size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                               int32_t D);
+
+/*
+ * Attention with rotary positions, KV-cache write and fused block mass.
+ *
+ * Computes, for every token t of every segment s and every query head h
+ * (KV head g = h / (Hq / Hkv)):
+ *   out[t,h,:] = sum_j softmax_j(sm_scale * q'[t,h,:] . K'[j,g,:]) V[j,g,:]
+ * over the keys j visible to t: the segment's ctx_len cached keys
+ * (positions 0..ctx-1) and its own tokens u with positions[u] <=
+ * positions[t]; with window > 0 only keys with position >
+ * positions[t] - window.  Keys of other segments are never visible (packed
+ * block-diagonal mask).  q' and K' are q and k rotated by their positions
+ * (rotate-half pairs (i, i + D/2), angle position * rope_theta^(-2i/D));
+ * rope_theta <= 0 disables the rotation.
+ *
+ * First writes the rotated K and V of every token t to the caches at
+ * slot_mapping[t]; attention then reads all keys through the caches.
+ *
+ * For every segment with score_flags[s] != 0 it also writes the block mass
+ *   block_mass[(cu_blocks[s] + b) * Hq + h] =
+ *     sum over rows t of the segment's last block (local rows
+ *     [(nb-1)*block_size, n)) of the softmax probability that row t, head h,
+ *     puts on the segment's own keys of block b
+ * (cached keys enter the softmax normaliser but are not scored).  Entries of
+ * unflagged segments are not written.
+ *
+ * dtype: UP_F32 (q, k, v, caches, out float32) or UP_BF16 (all bf16;
+ *        products on bf16 matrix cores, softmax and accumulation in fp32).
+ * Hq % Hkv == 0; D in {64, 128}.
+ * q [T, Hq, D], k, v [T, Hkv, D] row-major, read-only.
+ * k_cache, v_cache [num_pages, Hkv, page_size, D], read and written.
+ * sm_scale: logit scale; <= 0 selects 1/sqrt(D).
+ * score_flags [S] u8, may be NULL (no scoring); then cu_blocks and
+ *        block_mass may be NULL.  block_size as in up_block_offsets.
+ * block_mass [NB, Hq] f32 (NB = cu_blocks[S]).
+ * out [T, Hq, D] (dtype); lse [T, Hq] f32 natural-log normaliser of each
+ *        row's scaled logits, or NULL.
+ * workspace: at least up_attn_workspace_bytes(...) bytes, 16-byte aligned.
+ */
+up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                          int32_t D, const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, float rope_theta, int32_t window, float sm_scale,
+                          const uint8_t* score_flags, int32_t block_size,
+                          const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block scores: for a flagged segment s, score[b] = m_b / sum_b' m_b' with
+ * m_b = sum_h block_mass[b, h] (the importance of each own block,
+ * normalised over the segment).  Unflagged segments get score 0 for every
+ * block.  scores [NB] f32.
+ */
+up_status up_block_scores(const up_batch* batch, int32_t Hq, int32_t block_size,
+                          const int32_t* cu_blocks, const uint8_t* score_flags,
+                          const float* block_mass, float* scores, void* stream);
+
+/*
+ * Top-p block selection per flagged segment (review, Top-p Token Selection:
+ * the fewest blocks whose cumulative importance reaches p).  The first and
+ * last blocks are always kept and count toward p.  The others are taken in
+ * order of decreasing score (ties: lower block first) while the running sum
+ * is below the target.  Exact integer arithmetic: q_b = floor(score_b *
+ * 2^40), target = ceil(floor(p * 2^22 + 1/2) * sum_b q_b / 2^22); sums are
+ * order-independent, so the result does not depend on thread scheduling.
+ * p >= 1 keeps every block.  Scores must be finite, >= 0 and sum to < 2 per
+ * segment.  Unflagged segments keep all blocks.
+ * p: host double in [0, 1].  keep [NB] u8 (1 = kept); kept_blocks [S] i32
+ * number of kept blocks per segment (may be NULL).
+ */
+up_status up_topp_select(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                         const uint8_t* score_flags, double p, const float* scores,
+                         uint8_t* keep, int32_t* kept_blocks, void* stream);
+
+/* One row tensor to compact: rows of row_bytes bytes, [T, row] -> [T_kept, row]. */
+typedef struct up_rows {
+  const void* src;
+  void* dst;
+  int64_t row_bytes; /* > 0; 16-byte multiples with 16-byte aligned pointers copy fastest */
+} up_rows;
+
+/* Workspace bytes up_compact needs. */
+size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks);
+
+/*
+ * Compaction of the kept tokens (review, Method & Key Results: dropped
+ * tokens are removed from all later sublayers).  Token t of segment s is
+ * kept when its block (local index / block_size) has keep[cu_blocks[s] + b]
+ * != 0.  Outputs, in ascending original order:
+ *   index_map [T cap] i32: packed index of each kept token;
+ *   cu_seqlens_out [S+1] i32: per-segment kept counts, prefix-summed;
+ *   num_kept [1] i32 (device);
+ *   rows[i].dst[j] = rows[i].src[index_map[j]] byte for byte (positions and
+ *   KV slots are compacted by passing them as 4-byte row tensors).
+ * num_blocks (host): capacity >= cu_blocks[S].
+ * workspace: at least up_compact_workspace_bytes(S, num_blocks) bytes.
+ */
+up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                     const uint8_t* keep, int32_t num_blocks, int32_t n_rows,
+                     const up_rows* rows /* (host) array of n_rows */, int32_t* index_map,
+                     int32_t* cu_seqlens_out, int32_t* num_kept, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNIPREFILL_H */
