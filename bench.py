@@ -1,0 +1,211 @@
+"""Benchmark: packed prefill tokens/s of one operator call on one MI355X.
+
+Workload: the Llama-3.1-8B-shaped packed prefill (16 prompts, lengths
+uniform in [512, 8192] from seed 2, about 70K tokens; 32 query / 8 KV heads
+x 128, bf16; rotary base 500000; block 64, top-p 0.95; hidden width 4096).
+One step = the whole hot path on that batch: rotary embedding and paged
+KV-cache write, attention with the fused block mass, block scores, top-p
+selection and compaction of hidden states, positions and KV slots.  Inputs
+are synthetic and resident on the GPU before timing starts.
+
+Prints one JSON line.  ``roofline`` covers the attention kernel (the
+dominant one): algorithmic flops 4 * D * Hq * (causal in-segment query/key
+pairs) per launch over its average duration, timed with HIP events recorded
+by the library around that kernel on its stream.  ``cpu_baseline`` is the
+float64 NumPy oracle timed on this host on a sample of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "c2"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def algorithmic_pairs(call):
+    """Visible (query, key) pairs: cached keys plus the causal triangle."""
+    return sum(s.n * s.ctx + s.n * (s.n + 1) // 2 for s in call.segments)
+
+
+def traffic_from_profile(src_hash):
+    """HBM bytes per attention launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_c2_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel source sha256: ([0-9a-f]+)", txt)
+    t = re.search(r"HBM bytes per launch \(scaled\): ([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != src_hash:
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl, call, budget_s):
+    """Time the oracle on whole prompts of the batch, picked near the
+    token-weighted mean length (attention cost per token grows with length),
+    adding prompts until about ``budget_s`` of CPU work."""
+    import oracle
+    from oracle.prefill import default_threads
+    from workloads import to_f64
+
+    lens = np.array([s.n for s in call.segments])
+    wmean = float((lens ** 2).sum() / lens.sum())
+    order = np.argsort(np.abs(lens - wmean))
+    threads = default_threads()
+    done_tokens, spent, used = 0, 0.0, []
+    for i in order:
+        s = call.segments[int(i)]
+        a, b = int(call.cu_seqlens[i]), int(call.cu_seqlens[i + 1])
+        args = dict(segments=[(0, 0, s.n, True)], q=to_f64(call.q[a:b], "bf16"),
+                    k=to_f64(call.k[a:b], "bf16"), v=to_f64(call.v[a:b], "bf16"),
+                    positions=call.positions[a:b], cu_seqlens=[0, s.n], Hq=wl.Hq, Hkv=wl.Hkv,
+                    D=wl.D, theta=wl.theta, window=0, block_size=wl.block_size, p=wl.p,
+                    cache=oracle.KVCacheModel(),
+                    rows={"hidden": call.hidden[a:b], "positions": call.positions[a:b],
+                          "slot_mapping": call.slot_mapping[a:b]}, threads=threads)
+        t0 = time.perf_counter()
+        oracle.run_call(**args)
+        spent += time.perf_counter() - t0
+        done_tokens += s.n
+        used.append(s.n)
+        if spent >= budget_s:
+            break
+    return {"value": done_tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(used)} whole prompt(s) of the batch (lengths {used}, "
+                      f"{done_tokens} tokens) through rope, attention, scores, top-p and "
+                      f"compaction, float64 NumPy, {spent:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the operator is "
+              "built and measured for a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads as W
+    from block_sparse_token_amd import binding as B
+    from block_sparse_token_amd import step as ST
+
+    wl = W.make(WORKLOAD)
+    call = wl.calls[0]
+    dev = "cuda"
+    kc = torch.zeros((wl.num_pages, wl.Hkv, W.PAGE_SIZE, wl.D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
+                          call.block_table, device=dev)
+    rows = [("hidden", ST.stored_to_tensor(call.hidden, dev)),
+            ("positions", torch.from_numpy(call.positions.astype(np.int32)).to(dev)),
+            ("slot_mapping", torch.from_numpy(call.slot_mapping.astype(np.int32)).to(dev))]
+    pc = ST.PrefillCall(batch=batch, q=ST.stored_to_tensor(call.q, dev),
+                        k=ST.stored_to_tensor(call.k, dev), v=ST.stored_to_tensor(call.v, dev),
+                        k_cache=kc, v_cache=vc, num_blocks=call.num_blocks(wl.block_size),
+                        flags=torch.from_numpy(call.flags.astype(np.uint8)).to(dev),
+                        block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, rows=rows)
+    stream = torch.cuda.current_stream()
+    K, Wm = args.steps, args.warmup
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the underlying event
+        return e
+
+    for _ in range(Wm):
+        pc.launch()
+    torch.cuda.synchronize()
+    # per-step events: stage boundaries and the attention kernel itself
+    stage_ev = [[ev() for _ in range(5)] for _ in range(K)]
+    attn_ev = [(ev(), ev()) for _ in range(K)]
+    torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = stage_ev[i]
+        B.up_profile_attn_events(*attn_ev[i])
+        e[0].record(stream)
+        pc.attention()
+        e[1].record(stream)
+        pc.scores_stage()
+        e[2].record(stream)
+        pc.select_stage()
+        e[3].record(stream)
+        pc.compact_stage()
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.up_profile_attn_events()
+
+    ms_step = wall * 1e3 / K
+    T = call.T
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in attn_ev]))
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in stage_ev])
+    st_mean = st.mean(axis=0)
+    pairs = algorithmic_pairs(call)
+    flops = 4.0 * wl.D * wl.Hq * pairs
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    kept = int(pc.num_kept.item())
+    nb = call.num_blocks(wl.block_size)
+    W_bytes = wl.hidden_width * 2
+    compact_bytes = kept * (2 * W_bytes + 20) + nb
+    src = open(os.path.join(ROOT, "block_sparse_token_amd", "csrc", "attn_bf16.hip"), "rb").read()
+    src_hash = hashlib.sha256(src).hexdigest()
+    res = {
+        "metric": "packed prefill tokens/s (attn+score+select+compact) + % MFMA/HBM roofline",
+        "value": T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B-shaped packed prefill: 16 prompts U{512..8192} "
+                               f"(seed 2, {T} tokens), 32/8 heads x 128, bf16, rope 5e5, "
+                               "block 64, top-p 0.95, hidden 4096",
+                   "tokens": T, "segments": len(call.segments), "kept_tokens": kept},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile(src_hash),
+                     "kernel": "attn_bf16_kernel", "avg_ms": attn_ms,
+                     "flops_per_launch": flops, "pairs": pairs},
+        "stages_ms": {"rope_kv+plan+attention": float(st_mean[0]), "scores": float(st_mean[1]),
+                      "select": float(st_mean[2]), "compact": float(st_mean[3])},
+        "compact_hbm": {"bytes": compact_bytes,
+                        "GB/s": compact_bytes / (st_mean[3] * 1e-3) / 1e9,
+                        "frac": compact_bytes / (st_mean[3] * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -66,6 +66,7 @@ def lib():
             "up_block_scores": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
             "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
+            "up_profile_attn_events": (c_i32, [c_vp, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
         }
@@ -79,7 +80,7 @@ def lib():
 
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
-            "up_compact"]
+            "up_compact", "up_profile_attn_events"]
 
 
 def _check(st: int, what: str):
@@ -187,3 +188,11 @@ def up_compact(batch: Batch, block_size, cu_blocks, keep, num_blocks, rows, inde
                             len(rows), arr, _p(index_map), _p(cu_seqlens_out), _p(num_kept),
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)), "up_compact")
+
+
+def up_profile_attn_events(start=None, stop=None):
+    """Record torch.cuda.Event ``start``/``stop`` around the attention kernel
+    of later up_prefill_attn calls on this thread; no arguments turns it off."""
+    hs = ctypes.c_void_p(start.cuda_event) if start is not None else None
+    he = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+    _check(lib().up_profile_attn_events(hs, he), "up_profile_attn_events")

@@ -11,6 +11,7 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_attn_ev[2] = {nullptr, nullptr};
 
 up_status fail(up_status st, const char* fmt, ...) {
   char buf[512];
@@ -62,6 +63,14 @@ extern "C" {
 const char* up_last_error(void) { return g_err.c_str(); }
 
 const char* up_version(void) { return "uniprefill 0.1 gfx950"; }
+
+up_status up_profile_attn_events(void* attn_start, void* attn_stop) {
+  if ((attn_start == nullptr) != (attn_stop == nullptr))
+    return fail(UP_ERR_INVALID, "pass two events or none");
+  g_attn_ev[0] = reinterpret_cast<hipEvent_t>(attn_start);
+  g_attn_ev[1] = reinterpret_cast<hipEvent_t>(attn_stop);
+  return UP_OK;
+}
 
 up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
                            void* stream) {
@@ -179,8 +188,17 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   a.scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
   a.scale_log2 = (float)((double)a.scale * 1.4426950408889634073599246810018921);
   for (int j = 0; j < up::kMaxRopePairs; ++j) a.rope_rev[j] = rev[j];
+  if (g_attn_ev[0]) {
+    e = hipEventRecord(g_attn_ev[0], s);
+    if (e != hipSuccess) return device_status(e, "profiling event record");
+  }
   e = bf16 ? up::launch_attn_bf16(a, D, cap, s) : up::launch_attn_f32(a, D, cap, s);
-  return device_status(e, "attention launch");
+  if (e != hipSuccess) return device_status(e, "attention launch");
+  if (g_attn_ev[1]) {
+    e = hipEventRecord(g_attn_ev[1], s);
+    if (e != hipSuccess) return device_status(e, "profiling event record");
+  }
+  return UP_OK;
 }
 
 up_status up_block_scores(const up_batch* batch, int32_t Hq, int32_t block_size,

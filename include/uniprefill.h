@@ -209,6 +209,16 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
                      int32_t* cu_seqlens_out, int32_t* num_kept, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * Profiling aid (not part of the operator).  With both arguments non-NULL
+ * (hipEvent_t handles created by the caller), up_prefill_attn calls made
+ * afterwards on this thread record attn_start on their stream right before
+ * the attention kernel is launched and attn_stop right after it, so the
+ * kernel's own duration can be read with hipEventElapsedTime.  (NULL, NULL)
+ * turns it off.  The events must outlive the calls that record them.
+ */
+up_status up_profile_attn_events(void* attn_start, void* attn_stop);
+
 #ifdef __cplusplus
 }
 #endif
