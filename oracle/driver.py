@@ -59,3 +59,60 @@ def run_layer2(wl, call, res, threads=None):
                     Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, theta=wl.layer2["theta"],
                     window=wl.layer2["window"], block_size=wl.block_size, p=wl.p,
                     cache=KVCacheModel(), score=False, select=False, threads=threads)
+
+
+# --------------------------------------------------------------------------
+# sampled evaluation for full-size workloads
+# --------------------------------------------------------------------------
+def prompt_kv_before(wl, call_index, pid):
+    """Raw k, v and positions of prompt ``pid`` from the calls before
+    ``call_index`` (the tokens its cache holds), float64."""
+    ks, vs, ps = [], [], []
+    for call in wl.calls[:call_index]:
+        for i, s in enumerate(call.segments):
+            if s.prompt == pid:
+                a, b = int(call.cu_seqlens[i]), int(call.cu_seqlens[i + 1])
+                ks.append(to_f64(call.k[a:b], wl.dtype))
+                vs.append(to_f64(call.v[a:b], wl.dtype))
+                ps.append(np.asarray(call.positions[a:b], np.int64))
+    if not ks:
+        return None
+    return np.concatenate(ks), np.concatenate(vs), np.concatenate(ps)
+
+
+def sampled_segment(wl, call, si, rows, *, cached=None, theta=None, window=None,
+                    score=False, q=None, k=None, v=None, positions=None, cu=None, threads=None):
+    """Oracle outputs of segment ``si`` for local query rows ``rows`` and,
+    with ``score``, the segment's float32 block scores.
+
+    ``cached``: (K, V) float64 already rotated for positions 0..c-1, or None.
+    q/k/v/positions/cu default to the call's own arrays (layer 2 passes the
+    compacted ones)."""
+    from .prefill import apply_rope, attention, block_mass, normalise_scores
+
+    theta = wl.theta if theta is None else theta
+    window = wl.window if window is None else window
+    cu = call.cu_seqlens if cu is None else cu
+    a, b = int(cu[si]), int(cu[si + 1])
+    n = b - a
+    qa = to_f64((call.q if q is None else q)[a:b], wl.dtype)
+    ka = to_f64((call.k if k is None else k)[a:b], wl.dtype)
+    va = to_f64((call.v if v is None else v)[a:b], wl.dtype)
+    pos = np.asarray((call.positions if positions is None else positions)[a:b], np.int64)
+    k_rot = apply_rope(ka, pos, theta)
+    c = 0 if cached is None else cached[0].shape[0]
+    if c:
+        keys = np.concatenate([cached[0], k_rot])
+        vals = np.concatenate([cached[1], va])
+    else:
+        keys, vals = k_rot, va
+    k_pos = np.concatenate([np.arange(c, dtype=np.int64), pos])
+    rows = np.asarray(rows, np.int64)
+    q_rot = apply_rope(qa[rows], pos[rows], theta)
+    out, lse = attention(q_rot, keys, vals, pos[rows], k_pos, window, threads=threads)
+    res = {"rows": rows, "out": out, "lse": lse}
+    if score:
+        q_all = apply_rope(qa, pos, theta)
+        m = block_mass(q_all, keys, pos, k_pos, c, n, wl.block_size, window)
+        res["scores"] = normalise_scores(m).astype(np.float32)
+    return res

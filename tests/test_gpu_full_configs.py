@@ -1,0 +1,148 @@
+"""GPU parity at the five workloads' full sizes, launched as the benchmark
+launches them (same library calls, same buffers).
+
+The float64 oracle cannot redo 10^14 flops, so these tests check sampled
+query rows of every segment (first, last and seeded random rows), complete
+block scores of the listed segments, and - bit-exact - the selection (the
+oracle's top-p on the GPU scores) and the compaction of every call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle import driver
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def _rows(rng, n, k=6):
+    r = {0, n - 1}
+    if n > 2:
+        r.update(int(x) for x in rng.integers(0, n, size=k))
+    return sorted(r)
+
+
+def _check_segments(wl, call, g, cached_of, score_segs, rng, k_rows=6):
+    import gpu_harness as H
+    cu = call.cu_seqlens
+    cb = g["cu_blocks"]
+    for si, s in enumerate(call.segments):
+        rows = _rows(rng, s.n, k_rows)
+        do_score = s.flagged and si in score_segs
+        r = driver.sampled_segment(wl, call, si, rows, cached=cached_of(si, s), score=do_score)
+        got = g["out"][cu[si] + np.asarray(rows)]
+        H.check_out(wl.dtype, got, r["out"], f"segment {si} rows {rows[:4]}...")
+        if do_score:
+            H.check_scores(wl.dtype, g["scores"][cb[si]:cb[si + 1]], r["scores"])
+    H.check_selection_and_compaction(wl, call, g)
+
+
+def test_gpu_c2_full():
+    import gpu_harness as H
+    wl = W.make("c2")
+    call = wl.calls[0]
+    H.log(f"c2: T={call.T}")
+    kc, vc = H.make_caches(wl)
+    g = H.gpu_result(H.launch_call(wl, call, kc, vc))
+    H.log("c2: gpu done, checking")
+    _check_segments(wl, call, g, lambda si, s: None, set(range(len(call.segments))),
+                    np.random.default_rng(0))
+    H.log("c2: ok")
+
+
+def test_gpu_c3_full_chunked():
+    import gpu_harness as H
+    wl = W.make("c3")
+    kc, vc = H.make_caches(wl)
+    rng = np.random.default_rng(1)
+    check = {0, 1, 7, 15}
+    for ci, call in enumerate(wl.calls):
+        g = H.gpu_result(H.launch_call(wl, call, kc, vc))
+        if ci not in check:
+            # selection and compaction are checked bit-exact for every call
+            H.check_selection_and_compaction(wl, call, g)
+            continue
+        H.log(f"c3: call {ci} ctx={call.segments[0].ctx}")
+
+        def cached_of(si, s, ci=ci):
+            if s.ctx == 0:
+                return None
+            kk, vv, pp = driver.prompt_kv_before(wl, ci, s.prompt)
+            return oracle.apply_rope(kk, pp, wl.theta), vv
+
+        _check_segments(wl, call, g, cached_of, {0}, rng, k_rows=4)
+    H.log("c3: ok")
+
+
+def test_gpu_c4_full_mixed_step():
+    import gpu_harness as H
+    wl = W.make("c4")
+    call = wl.calls[0]
+    H.log(f"c4: T={call.T} segments={len(call.segments)}")
+    kc, vc = H.make_caches(wl)
+    g = H.gpu_result(H.launch_call(wl, call, kc, vc))
+    H.log("c4: gpu done")
+    n_dec = sum(1 for s in call.segments if not s.flagged)
+    rng = np.random.default_rng(2)
+    ctxs = [s.ctx for s in call.segments[:n_dec]]
+    pick = {int(np.argmax(ctxs)), int(np.argmin(ctxs))}
+    pick.update(int(x) for x in rng.choice(n_dec, size=10, replace=False))
+    cu = call.cu_seqlens
+    for si in sorted(pick):
+        s = call.segments[si]
+        K, V = H.read_back_cache(wl, kc, vc, s.prompt, s.ctx)
+        r = driver.sampled_segment(wl, call, si, [0],
+                                   cached=(W.to_f64(K, "bf16"), W.to_f64(V, "bf16")))
+        H.check_out("bf16", g["out"][cu[si]:cu[si] + 1], r["out"], f"decode {si} ctx {s.ctx}")
+    for si in range(n_dec, len(call.segments)):
+        s = call.segments[si]
+        rows = _rows(rng, s.n, 8)
+        r = driver.sampled_segment(wl, call, si, rows, score=True)
+        H.check_out("bf16", g["out"][cu[si] + np.asarray(rows)], r["out"], f"prefill {si}")
+        H.check_scores("bf16", g["scores"][g["cu_blocks"][si]:g["cu_blocks"][si + 1]],
+                       r["scores"])
+    H.check_selection_and_compaction(wl, call, g)
+    H.log("c4: ok")
+
+
+def test_gpu_c5_full_with_sliding_window_layer():
+    import gpu_harness as H
+    from block_sparse_token_amd import step as ST
+    wl = W.make("c5")
+    call = wl.calls[0]
+    H.log(f"c5: T={call.T}")
+    kc, vc = H.make_caches(wl)
+    pc = H.launch_call(wl, call, kc, vc)
+    g = H.gpu_result(pc)
+    H.log("c5: layer 1 done")
+    rng = np.random.default_rng(3)
+    _check_segments(wl, call, g, lambda si, s: None, set(range(len(call.segments))), rng)
+    # layer 2: sliding window over the kept tokens at their original positions,
+    # K/V written at the compacted slots of a second cache
+    nk = g["num_kept"]
+    S = len(call.segments)
+    batch2 = ST.B.Batch(pc.cu_seqlens_out, torch.zeros(S, dtype=torch.int32, device="cuda"),
+                        pc.rows_out["positions"][:nk].contiguous(),
+                        pc.rows_out["slot_mapping"][:nk].contiguous(), None)
+    kc2, vc2 = torch.zeros_like(kc), torch.zeros_like(vc)
+    l2 = ST.PrefillCall(batch=batch2, q=pc.rows_out["q2"][:nk].contiguous(),
+                        k=pc.rows_out["k2"][:nk].contiguous(),
+                        v=pc.rows_out["v2"][:nk].contiguous(), k_cache=kc2, v_cache=vc2,
+                        num_blocks=1, flags=None, block_size=wl.block_size, p=wl.p,
+                        rope_theta=wl.layer2["theta"], window=wl.layer2["window"])
+    l2.launch()
+    torch.cuda.synchronize()
+    out2 = ST.tensor_to_stored(l2.out)
+    H.log(f"c5: layer 2 done on {nk} kept tokens")
+    ro = g["rows_out"]
+    cu2 = g["cu_seqlens_out"]
+    for si in range(S):
+        n2 = int(cu2[si + 1] - cu2[si])
+        rows = _rows(rng, n2, 6)
+        r = driver.sampled_segment(wl, call, si, rows, theta=wl.layer2["theta"],
+                                   window=wl.layer2["window"], q=ro["q2"], k=ro["k2"],
+                                   v=ro["v2"], positions=ro["positions"], cu=cu2)
+        H.check_out("bf16", out2[cu2[si] + np.asarray(rows)], r["out"], f"layer2 segment {si}")
+    H.log("c5: ok")
