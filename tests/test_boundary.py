@@ -1,0 +1,124 @@
+"""The C-ABI library on the CPU: it loads without a GPU, exports every entry
+point the header declares, and rejects bad arguments on the host before any
+launch (no GPU call is made by these tests: every call below fails
+validation)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+
+import block_sparse_token_amd as bst
+from block_sparse_token_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uniprefill.h")
+
+UP_OK, UP_ERR_INVALID, UP_ERR_UNSUPPORTED, UP_ERR_WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(up_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(Bd.LIB_PATH):
+        pytest.skip("library not built")
+    return Bd.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", Bd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (up_[a-z_0-9]+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        getattr(L, n)
+    assert set(Bd.EXPORTED) == set(names)
+    assert "gfx950" in bst.up_version()
+
+
+def _batch(S=2, T=10, page_size=16, with_ptrs=True):
+    b = Bd.UpBatch()
+    b.num_seqs, b.num_tokens = S, T
+    if with_ptrs:
+        b.cu_seqlens = b.ctx_lens = b.positions = b.slot_mapping = b.block_table = FAKE.value
+    b.max_pages, b.page_size = 4, page_size
+    return b
+
+
+def _attn(L, b, *, dtype=1, Hq=8, Hkv=2, D=128, ws_bytes=1 << 20, flags=None, block=64,
+          theta=1e4, scale=0.0):
+    return L.up_prefill_attn(ctypes.byref(b) if b is not None else None, dtype, Hq, Hkv, D,
+                             FAKE, FAKE, FAKE, FAKE, FAKE, theta, 0, scale, flags, block, FAKE,
+                             FAKE, FAKE, None, FAKE, ws_bytes, None)
+
+
+def test_attention_argument_validation(L):
+    b = _batch()
+    assert _attn(L, None) == UP_ERR_INVALID
+    assert _attn(L, b, Hq=6, Hkv=4) == UP_ERR_INVALID
+    assert _attn(L, b, Hq=12, Hkv=4) == UP_ERR_UNSUPPORTED  # G = 3
+    assert _attn(L, b, D=96) == UP_ERR_UNSUPPORTED
+    assert _attn(L, b, dtype=7) == UP_ERR_UNSUPPORTED
+    assert _attn(L, _batch(page_size=8)) == UP_ERR_UNSUPPORTED
+    assert _attn(L, _batch(S=0)) == UP_ERR_INVALID
+    assert _attn(L, _batch(S=5, T=3)) == UP_ERR_INVALID
+    assert _attn(L, b, flags=FAKE, block=48) == UP_ERR_UNSUPPORTED
+    assert _attn(L, b, theta=float("nan")) == UP_ERR_INVALID
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128)
+    assert need > 16
+    assert _attn(L, b, ws_bytes=need - 1) == UP_ERR_WORKSPACE
+    assert b"workspace" in L.up_last_error()
+    nb = _batch(with_ptrs=False)
+    assert _attn(L, nb) == UP_ERR_INVALID
+    assert b"NULL" in L.up_last_error()
+
+
+def test_workspace_size_arithmetic(L):
+    b = _batch(S=16, T=70000)
+    # bf16: 256 packed rows per tile -> 64 positions at GQA 4; one int2 per item
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128)
+    assert need == 16 + 8 * (math.ceil(70000 / 64) + 2 * 16 + 1)
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128) == 0
+    assert L.up_compact_workspace_bytes(16, 1100) == 8 * (1100 + 4)
+    assert L.up_compact_workspace_bytes(16, 0) == 0
+
+
+def test_select_scores_compact_validation(L):
+    b = _batch()
+    bp = ctypes.byref(b)
+    assert L.up_topp_select(bp, 64, FAKE, FAKE, 1.5, FAKE, FAKE, None, None) == UP_ERR_INVALID
+    assert L.up_topp_select(bp, 64, FAKE, FAKE, -0.1, FAKE, FAKE, None, None) == UP_ERR_INVALID
+    assert L.up_topp_select(bp, 64, FAKE, FAKE, float("nan"), FAKE, FAKE, None, None) == UP_ERR_INVALID
+    assert L.up_topp_select(bp, 24, FAKE, FAKE, 0.5, FAKE, FAKE, None, None) == UP_ERR_UNSUPPORTED
+    assert L.up_topp_select(bp, 64, None, FAKE, 0.5, FAKE, FAKE, None, None) == UP_ERR_INVALID
+    assert L.up_block_scores(bp, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == UP_ERR_INVALID
+    assert L.up_block_scores(bp, 8, 64, FAKE, FAKE, None, FAKE, None) == UP_ERR_INVALID
+    assert L.up_block_offsets(bp, 100, FAKE, None) == UP_ERR_UNSUPPORTED
+    rows = (Bd.UpRows * 1)(Bd.UpRows(FAKE.value, FAKE.value, 0))
+    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                        None) == UP_ERR_INVALID  # row_bytes 0
+    rows = (Bd.UpRows * 1)(Bd.UpRows(FAKE.value, FAKE.value, 8))
+    assert L.up_compact(bp, 64, FAKE, FAKE, 1, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                        None) == UP_ERR_INVALID  # fewer blocks than segments
+    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 8,
+                        None) == UP_ERR_WORKSPACE
+    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 99, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                        None) == UP_ERR_UNSUPPORTED
+    assert L.up_profile_attn_events(FAKE, None) == UP_ERR_INVALID
+    assert L.up_profile_attn_events(None, None) == UP_OK
+
+
+def test_binding_refuses_host_tensors():
+    t = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(Bd.UniprefillError):
+        Bd.Batch(t, t, t, t)
