@@ -21,7 +21,11 @@
 //  * Key tiles of 64 go through a three-stage pipeline: cache-row indices
 //    (page table or per-token slot) two tiles ahead, K/V data one tile ahead
 //    in registers, and a double-buffered LDS stage, one barrier per tile.
-//    Waves 0-3 fetch K rows, waves 4-7 fetch V and transpose it into LDS.
+//    Eight threads stage each key (four move a quarter of its K row, four a
+//    quarter of its V row); V stays row-major in LDS and its V^T fragments
+//    come from ds_read_b64_tr_b16 transpose reads.
+//  * Online softmax in exp2 with the scale folded in and a lazily raised
+//    running max (rescale only when a tile's max is 2^8 above it).
 //  * Score items: for a scored segment and KV head, a first QK^T sweep over
 //    every visible key gives the exact softmax normaliser of the rows of the
 //    segment's last query block; a second sweep over the segment's own keys
@@ -34,6 +38,13 @@ namespace up {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// native vector for staged 16-byte chunks (HIP's uint4 is a struct with a
+// union, which the optimiser may leave on the stack)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// global-address-space views, so loads from computed addresses stay global_load
+// (a flat load would also hold the LDS counter the compute phase waits on)
+typedef __attribute__((address_space(1))) const u32x4 gu32x4;
+typedef __attribute__((address_space(1))) const int gint;
 
 template <int D_>
 struct Cfg {
@@ -44,17 +55,24 @@ struct Cfg {
   static constexpr int BN = 64;             // keys per tile
   static constexpr int KC = D / 16;         // 16-wide d steps (QK^T)
   static constexpr int DB = D / 32;         // 32-wide d blocks (PV)
-  static constexpr int KSTR = D * 2 + 16;   // LDS bytes per K row
-  static constexpr int VSTR = BN * 2 + 16;  // LDS bytes per V^T row
+  // LDS row strides (bytes).  K rows are read 16 bytes per lane, 32 rows at a
+  // time: a stride of 4 banks mod 64 keeps 16 lanes on distinct banks.  V rows
+  // are read with ds_read_b64_tr_b16 (4 rows x 32 bytes per 16 lanes, two
+  // groups per cycle): a stride of 16 banks mod 64 keeps those disjoint.
+  static constexpr int KSTR = D * 2 + 16;
+  static constexpr int VSTR = 320;
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = K_OFF + BN * KSTR;
-  static constexpr int POS_OFF = V_OFF + D * VSTR;
+  static constexpr int POS_OFF = V_OFF + BN * VSTR;
   static constexpr int BUF_BYTES = POS_OFF + BN * 4;
   static constexpr int RED_OFF = 2 * BUF_BYTES;
   static constexpr int RED_BYTES = NW * 4 * 32 * 4;  // [wave][block in tile][head] f32
   static constexpr int MISC_OFF = RED_OFF + RED_BYTES;
   static constexpr int LDS_BYTES = MISC_OFF + 64;
-  static constexpr int KCH = D / 32;  // 16-byte chunks of K per loader thread per tile
+  // loaders: 8 threads per key; parts 0-3 move a quarter K row, 4-7 a quarter V row
+  static constexpr int PART_BYTES = D / 2;
+  static constexpr int PCH = PART_BYTES / 16;  // 16-byte chunks per thread (2 or 4)
+  static_assert(VSTR >= D * 2, "V row stride");
 };
 
 constexpr int kPosInvalid = 0x7fffffff;
@@ -63,21 +81,6 @@ constexpr float kNegBig = -1.0e30f;
 struct Seg {
   int s, q0, n, c;
 };
-
-// Row index (page * Hkv + g) * 16 + offset of virtual key u: cached keys
-// through the page table, own keys through their slots.
-__device__ inline int cache_row(const AttnArgs& a, const Seg& sg, int g, int u) {
-  int page, off;
-  if (u < sg.c) {
-    page = a.block_table[(long)sg.s * a.max_pages + (u >> 4)];
-    off = u & 15;
-  } else {
-    const int slot = a.slot_mapping[sg.q0 + u - sg.c];
-    page = slot >> 4;
-    off = slot & 15;
-  }
-  return (page * a.Hkv + g) * kPageSize + off;
-}
 
 __device__ inline int key_position(const AttnArgs& a, const Seg& sg, int u) {
   return u < sg.c ? u : a.positions[sg.q0 + u - sg.c];
@@ -115,97 +118,62 @@ __device__ inline int first_key_at_or_after(const AttnArgs& a, const Seg& sg, in
 // ----------------------------------------------------------------------------
 // tile pipeline: indices -> registers -> LDS
 // ----------------------------------------------------------------------------
-// key index within a 16-key step -> LDS column of V^T (quads 0,1,2,3 -> 0,2,1,3)
-__device__ inline int vt_col(int kk) {
-  const int q = (kk >> 2) & 3;
-  const int cq = ((q & 1) << 1) | (q >> 1);
-  return (kk & ~15) | (cq << 2) | (kk & 3);
-}
-
+// Thread t stages key t/8 of the tile: parts 0-3 a quarter of its K row,
+// parts 4-7 a quarter of its V row.  Keys past the visible range are clamped
+// to the last visible one (real, finite data) and get position INT_MAX so the
+// mask removes them; no branch depends on per-key data.
 template <class C, bool kWithV>
 struct Pipe {
-  int row[4];  // cache rows (K loaders use row[0]); -1 = beyond the visible range
-  int ipos;    // key position from the index stage (K loaders with part 0)
-  int dpos;    // the same, latched with the data stage
-  uint4 d[4];  // staged data
+  int row;    // cache row (page * Hkv + g) * 16 + offset
+  int ipos;   // key position from the index stage
+  int dpos;   // the same, latched with the data stage
+  u32x4 d0, d1, d2, d3;  // staged data (d2, d3 unused when D = 64)
 
   __device__ inline void index(const AttnArgs& a, const Seg& sg, int g, int u0, int u_end) {
-    const int tid = threadIdx.x;
-    if (tid < 256) {
-      const int u = u0 + (tid >> 2);
-      const bool ok = u < u_end;
-      row[0] = ok ? cache_row(a, sg, g, u) : -1;
-      if ((tid & 3) == 0) ipos = ok ? key_position(a, sg, u) : kPosInvalid;
-    } else if (kWithV) {
-      const int t2 = tid - 256;
-      if (t2 < 2 * C::D) {
-        const int quad = (t2 & 63) >> 2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int u = u0 + quad * 4 + e;
-          row[e] = u < u_end ? cache_row(a, sg, g, u) : -1;
-        }
-      }
-    }
+    const int kk = threadIdx.x >> 3;
+    const int u = u0 + kk;
+    const int uu = min(u, u_end - 1);
+    const bool cached = uu < sg.c;
+    const int own = max(uu - sg.c, 0);
+    // select the index address arithmetically (a select of two kernel-argument
+    // pointers would be turned into a per-lane load of the argument itself)
+    const uintptr_t bt = (uintptr_t)(a.block_table + (long)sg.s * a.max_pages + (uu >> 4));
+    const uintptr_t sm = (uintptr_t)(a.slot_mapping + sg.q0 + own);
+    const int val = *(gint*)(cached ? bt : sm);
+    const int page = cached ? val : (val >> 4);
+    const int off = cached ? (uu & 15) : (val & 15);
+    row = (page * a.Hkv + g) * kPageSize + off;
+    const int opos = a.positions[sg.q0 + min(own, sg.n - 1)];
+    ipos = u < u_end ? (cached ? uu : opos) : kPosInvalid;
   }
 
+  // Loads and stores are unconditional (a K-only sweep moves V too, unused),
+  // so the staged registers never live across divergent control flow.
   __device__ inline void load(const AttnArgs& a) {
-    const int tid = threadIdx.x;
-    if (tid < 256) {
-      const int part = tid & 3;
-      dpos = ipos;
-      if (row[0] >= 0) {
-        const uint4* src =
-            (const uint4*)((const uint16_t*)a.k_cache + (long)row[0] * C::D + part * (C::D / 4));
-#pragma unroll
-        for (int i = 0; i < C::KCH; ++i) d[i] = src[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < C::KCH; ++i) d[i] = make_uint4(0, 0, 0, 0);
-      }
-    } else if (kWithV) {
-      const int t2 = tid - 256;
-      if (t2 < 2 * C::D) {
-        const int octet = (t2 >> 6) * 4 + (t2 & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          d[e] = row[e] >= 0
-                     ? *(const uint4*)((const uint16_t*)a.v_cache + (long)row[e] * C::D + octet * 8)
-                     : make_uint4(0, 0, 0, 0);
-      }
+    const int part = threadIdx.x & 7;
+    dpos = ipos;
+    const uintptr_t kb = (uintptr_t)a.k_cache, vb = (uintptr_t)a.v_cache;
+    const uintptr_t base = kb + (uintptr_t)(part >> 2) * (vb - kb);
+    gu32x4* src = (gu32x4*)(base + ((long)row * C::D + (part & 3) * (C::PART_BYTES / 2)) * 2);
+    d0 = src[0];
+    d1 = src[1];
+    if constexpr (C::PCH == 4) {
+      d2 = src[2];
+      d3 = src[3];
     }
   }
 
   __device__ inline void store(char* buf) const {
-    const int tid = threadIdx.x;
-    if (tid < 256) {
-      const int kk = tid >> 2, part = tid & 3;
-      uint4* dst = (uint4*)(buf + C::K_OFF + kk * C::KSTR + part * (C::D / 2));
-#pragma unroll
-      for (int i = 0; i < C::KCH; ++i) dst[i] = d[i];
-      if (part == 0) ((int*)(buf + C::POS_OFF))[kk] = dpos;
-    } else if (kWithV) {
-      const int t2 = tid - 256;
-      if (t2 < 2 * C::D) {
-        const int quad = (t2 & 63) >> 2, octet = (t2 >> 6) * 4 + (t2 & 3);
-        const int col = vt_col(quad * 4);  // 4 consecutive keys stay together
-        const uint32_t w0[4] = {d[0].x, d[0].y, d[0].z, d[0].w};
-        const uint32_t w1[4] = {d[1].x, d[1].y, d[1].z, d[1].w};
-        const uint32_t w2[4] = {d[2].x, d[2].y, d[2].z, d[2].w};
-        const uint32_t w3[4] = {d[3].x, d[3].y, d[3].z, d[3].w};
-        // d[e] holds d-values octet*8 .. +7 of key quad*4 + e; write V^T[d][col + e]
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          uint2 lo, hi;
-          lo.x = (w0[x] & 0xffffu) | (w1[x] << 16);
-          lo.y = (w2[x] & 0xffffu) | (w3[x] << 16);
-          hi.x = (w0[x] >> 16) | (w1[x] & 0xffff0000u);
-          hi.y = (w2[x] >> 16) | (w3[x] & 0xffff0000u);
-          *(uint2*)(buf + C::V_OFF + (octet * 8 + 2 * x) * C::VSTR + col * 2) = lo;
-          *(uint2*)(buf + C::V_OFF + (octet * 8 + 2 * x + 1) * C::VSTR + col * 2) = hi;
-        }
-      }
+    const int kk = threadIdx.x >> 3, part = threadIdx.x & 7;
+    char* dst = part < 4 ? buf + C::K_OFF + kk * C::KSTR + part * C::PART_BYTES
+                         : buf + C::V_OFF + kk * C::VSTR + (part - 4) * C::PART_BYTES;
+    ((u32x4*)dst)[0] = d0;
+    ((u32x4*)dst)[1] = d1;
+    if constexpr (C::PCH == 4) {
+      ((u32x4*)dst)[2] = d2;
+      ((u32x4*)dst)[3] = d3;
     }
+    if (part == 0) ((int*)(buf + C::POS_OFF))[kk] = dpos;
   }
 };
 
@@ -341,6 +309,22 @@ __device__ inline int window_start(const AttnArgs& a, const Seg& sg, int pos_fir
 // ----------------------------------------------------------------------------
 // attention item: one query tile of one segment, one KV head
 // ----------------------------------------------------------------------------
+// Row max over this lane's 32 keys and its partner lane's, scaled to log2 units.
+__device__ inline float scaled_row_max(const f32x16 (&s)[2], float sl2) {
+  float mx = kNegBig;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mb][e]);
+  return pair_max(mx) * sl2;
+}
+
+// The running max is only raised (and O, l rescaled) when a tile's max
+// exceeds it by more than kLazy (log2 units); probabilities are computed
+// against the stale max and stay below 2^kLazy, exact after the final
+// division by l.
+constexpr float kLazy = 8.0f;
+
 template <class C>
 __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5;
@@ -365,16 +349,16 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const int pos_last = a.positions[sg.q0 + i_last];
   const int u_end = sg.c + i_last + 1;
   const int u_lo = window_start(a, sg, pos_first, lds, C::MISC_OFF);
+  const int window = a.window;
+  const int full_limit = sg.c + i_first;
+  const float sl2 = a.scale_log2;
 
   f32x16 o[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float m = kNegBig, lsum = 0.f;
-  const float sl2 = a.scale_log2;
-  const int window = a.window;
-  const int full_limit = sg.c + i_first;
+  float ms = kNegBig, lsum = 0.f;  // running max (log2 units) and partial row sum
 
   sweep<C, true>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds, [&](const char* buf, int u0) {
     f32x16 sacc[2];
@@ -382,41 +366,43 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
     const int kpos0 = ((const int*)(buf + C::POS_OFF))[0];
     const bool full = (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos0 > pos_last - window);
     if (!full) apply_mask<C>(buf, qpos, window, sacc);
-    float mx = kNegBig;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mb][e]);
-    mx = pair_max(mx);
-    const float mnew = fmaxf(m, mx);
-    if (__any(mnew > m)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * sl2);
+    const float mx = scaled_row_max(sacc, sl2);
+    if (__any(mx > ms + kLazy)) {
+      const float mnew = fmaxf(ms, mx);
+      const float alpha = __builtin_amdgcn_exp2f(ms - mnew);
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      m = mnew;
+      ms = mnew;
     }
-    const float mb2 = m * sl2;
     float rs = 0.f;
     bf16x8 pf[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[mb][e] * sl2 - mb2);
-        rs += p;
-        pf[mb * 2 + (e >> 3)][e & 7] = (__bf16)p;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -ms));
+        rs += pv;
+        pf[mb * 2 + (e >> 3)][e & 7] = (__bf16)pv;
       }
     lsum += rs;
-    // O^T += V^T P^T; 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2
+    // O^T += V^T P^T; 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2.
+    // V^T fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 + 0..3 and
+    // ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which lane
+    // 4a+b of each 16-lane group points at V[key0 + a][d0 + 4b].
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)(buf + C::V_OFF + (db * 32 + (l & 31)) * C::VSTR +
-                                           (ks * 16 + h * 8) * 2);
+        const char* vp = buf + C::V_OFF + (ks * 16 + h * 4 + ((l & 15) >> 2)) * C::VSTR +
+                         (db * 32 + (l & 16) + 4 * (l & 3)) * 2;
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(vp));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(vp + 8 * C::VSTR));
+        const bf16x8 vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
     }
@@ -436,7 +422,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(o[db][jg * 4 + e] * inv);
       *(bf16x4*)(out + qrow + db * 32 + jg * 8 + h * 4) = v4;
     }
-  if (a.lse && h == 0) a.lse[qrow / C::D] = (m * sl2 + __log2f(ltot)) * 0.69314718055994530942f;
+  if (a.lse && h == 0) a.lse[qrow / C::D] = (ms + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
 // ----------------------------------------------------------------------------

@@ -10,7 +10,7 @@ namespace up {
 
 // ---------------------------------------------------------------- limits
 constexpr int kPageSize = 16;
-constexpr int kMaxSeqsPlan = 8192;  // segments per call the work planner handles
+constexpr int kMaxSeqsPlan = 4096;  // segments per call the work planner handles
 constexpr int kMaxRopePairs = 64;   // D / 2 for D = 128
 
 // ---------------------------------------------------------------- work items

@@ -1,9 +1,7 @@
 // Batch metadata kernels: block offsets and the attention work list.
 //
-// The work list orders query tiles by decreasing cost (keys each tile's last
-// row can see) so the longest tiles start first and the tail of the launch
-// holds the short ones.  Score items (two QK^T sweeps over a segment's last
-// query block) go first.
+// The work list puts score items (two QK^T sweeps over a segment's last
+// query block) first, then query tiles segment by segment.
 #include "common.h"
 
 namespace up {
@@ -49,42 +47,54 @@ hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size
   return hipGetLastError();
 }
 
-constexpr int kBuckets = 2048;  // cost buckets of 64 keys; the last one is open-ended
-
-__device__ inline int tile_cost(int c, int n, int P, int j, int window) {
-  int last_row = min((j + 1) * P, n);  // rows [jP, last_row)
-  int vis = c + last_row;
-  if (window > 0) vis = min(vis, window + P);
-  return vis;
-}
-
-// One workgroup.  Segment tile prefix sums live in LDS (S <= kMaxSeqsPlan).
+// One workgroup.  Segments are ranked by the visible-key count of their last
+// row (ctx + n, or the window), heaviest first, ties by index; items are
+// written segment by segment, each segment's tiles from the last (most keys)
+// to the first.  Neighbouring items then read the same segment's keys, so
+// the workgroups that run together on one XCD share its L2, and the longest
+// tiles still start first.  Score items precede all tiles.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu_seqlens,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const uint8_t* __restrict__ score_flags,
                                                     int S, int P, int window,
                                                     int2* __restrict__ items,
                                                     int32_t* __restrict__ count, int capacity) {
+  __shared__ int32_t key[kMaxSeqsPlan];
+  __shared__ int32_t order[kMaxSeqsPlan];
   __shared__ int32_t cu_t[kMaxSeqsPlan + 1];
-  __shared__ int32_t hist[kBuckets];
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry, n_score;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  for (int b = tid; b < kBuckets; b += 1024) hist[b] = 0;
   if (tid == 0) {
     carry = 0;
     n_score = 0;
     cu_t[0] = 0;
   }
+  for (int s = tid; s < S; s += 1024) {
+    const int n = cu_seqlens[s + 1] - cu_seqlens[s];
+    int k = ctx_lens[s] + n;
+    if (window > 0) k = min(k, window + P);
+    key[s] = k;
+  }
   __syncthreads();
-  // tiles per segment, prefix-summed; count flagged segments
+  for (int s = tid; s < S; s += 1024) {
+    const int ks = key[s];
+    int r = 0;
+    for (int t = 0; t < S; ++t) {
+      const int kt = key[t];
+      r += (kt > ks) || (kt == ks && t < s);
+    }
+    order[r] = s;
+    if (score_flags && score_flags[s]) atomicAdd(&n_score, 1);
+  }
+  __syncthreads();
+  // tiles per segment in rank order, prefix-summed
   for (int base = 0; base < S; base += 1024) {
-    const int s = base + tid;
+    const int r = base + tid;
     int v = 0;
-    if (s < S) {
-      const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-      v = (n + P - 1) / P;
-      if (score_flags && score_flags[s]) atomicAdd(&n_score, 1);
+    if (r < S) {
+      const int s = order[r];
+      v = (cu_seqlens[s + 1] - cu_seqlens[s] + P - 1) / P;
     }
     int x = v;
 #pragma unroll
@@ -96,57 +106,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
     int off = carry;
     for (int w = 0; w < wid; ++w) off += wsum[w];
-    if (s < S) cu_t[s + 1] = off + x;
+    if (r < S) cu_t[r + 1] = off + x;
     __syncthreads();
     if (tid == 1023) carry = off + x;
     __syncthreads();
   }
   const int n_tiles = cu_t[S];
   const int ns = n_score;
-  int total = n_tiles + ns;
-  if (total > capacity) total = capacity;  // cannot happen for a valid batch
-  // score items first, in segment order
   if (tid == 0) {
     int k = 0;
     if (score_flags)
-      for (int s = 0; s < S && k < ns; ++s)
-        if (score_flags[s]) items[k++] = make_int2(s, kScoreTile);
-    *count = total;
+      for (int r = 0; r < S && k < ns; ++r)
+        if (score_flags[order[r]]) items[k++] = make_int2(order[r], kScoreTile);
+    *count = min(n_tiles + ns, capacity);
   }
-  // histogram of tile costs
   for (int i = tid; i < n_tiles; i += 1024) {
-    int lo = 0, hi = S - 1;  // find s with cu_t[s] <= i < cu_t[s+1]
+    int lo = 0, hi = S - 1;  // rank r with cu_t[r] <= i < cu_t[r+1]
     while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
+      const int mid = (lo + hi + 1) >> 1;
       if (cu_t[mid] <= i) lo = mid; else hi = mid - 1;
     }
-    const int s = lo, j = i - cu_t[s];
-    const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-    const int b = min(kBuckets - 1, tile_cost(ctx_lens[s], n, P, j, window) >> 6);
-    atomicAdd(&hist[b], 1);
-  }
-  __syncthreads();
-  // exclusive scan in decreasing-cost order: offset[b] = ns + sum_{b' > b} hist[b']
-  if (tid == 0) {
-    int acc = ns;
-    for (int b = kBuckets - 1; b >= 0; --b) {
-      int h = hist[b];
-      hist[b] = acc;
-      acc += h;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < n_tiles; i += 1024) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (cu_t[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int s = lo, j = i - cu_t[s];
-    const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-    const int b = min(kBuckets - 1, tile_cost(ctx_lens[s], n, P, j, window) >> 6);
-    const int slot = atomicAdd(&hist[b], 1);
-    if (slot < capacity) items[slot] = make_int2(s, j);
+    const int s = order[lo];
+    const int nt = cu_t[lo + 1] - cu_t[lo];
+    const int j = nt - 1 - (i - cu_t[lo]);
+    if (ns + i < capacity) items[ns + i] = make_int2(s, j);
   }
 }
 
