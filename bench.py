@@ -54,7 +54,7 @@ def algorithmic_pairs(call):
 def traffic_from_profile(src_hash):
     """HBM bytes per attention launch from the committed counter summary,
     if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "attn_bf16_c2_counters.md")
+    path = os.path.join(ROOT, "profiles", "attn_bf16_packed_llama8b_counters.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
