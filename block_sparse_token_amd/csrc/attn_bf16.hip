@@ -16,14 +16,15 @@
 //  * A wave owns 32 packed rows.  S^T = K Q^T and O^T = V^T P^T run on
 //    v_mfma_f32_32x32x16_bf16: the S^T accumulator holds, per lane, 16 keys
 //    of one query row, which is the B-operand layout P^T needs once keys are
-//    permuted within each 16-key step (V^T is stored in LDS with the same
-//    permutation).  Row statistics (max, sum) live in one lane pair (l, l^32).
-//  * Key tiles of 64 go through a three-stage pipeline: cache-row indices
-//    (page table or per-token slot) two tiles ahead, K/V data one tile ahead
-//    in registers, and a double-buffered LDS stage, one barrier per tile.
-//    Eight threads stage each key (four move a quarter of its K row, four a
-//    quarter of its V row); V stays row-major in LDS and its V^T fragments
-//    come from ds_read_b64_tr_b16 transpose reads.
+//    permuted within each 16-key step; V^T fragments come from
+//    ds_read_b64_tr_b16 transpose reads of row-major V.  Row statistics (max,
+//    sum) live in one lane pair (l, l^32).
+//  * Key tiles of 64 arrive by direct global->LDS copies (no staging
+//    registers): the cache-row index and position of every key four tiles
+//    ahead go to a small LDS ring, the K and V rows two tiles ahead go to one
+//    of three tile buffers.  Each wave waits only for its own copies of the
+//    next tile (an exact count of its outstanding copies), then one barrier
+//    per tile publishes it.
 //  * Online softmax in exp2 with the scale folded in and a lazily raised
 //    running max (rescale only when a tile's max is 2^8 above it).
 //  * Score items: for a scored segment and KV head, a first QK^T sweep over
@@ -37,43 +38,64 @@ namespace up {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-// native vector for staged 16-byte chunks (HIP's uint4 is a struct with a
-// union, which the optimiser may leave on the stack)
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// global-address-space views, so loads from computed addresses stay global_load
-// (a flat load would also hold the LDS counter the compute phase waits on)
-typedef __attribute__((address_space(1))) const u32x4 gu32x4;
-typedef __attribute__((address_space(1))) const int gint;
+typedef __attribute__((address_space(3))) const char lchar;
 
 template <int D_>
 struct Cfg {
   static constexpr int D = D_;
   static constexpr int NW = 8;
   static constexpr int THREADS = NW * 64;
-  static constexpr int ROWS = 32 * NW;      // packed rows per workgroup
-  static constexpr int BN = 64;             // keys per tile
-  static constexpr int KC = D / 16;         // 16-wide d steps (QK^T)
-  static constexpr int DB = D / 32;         // 32-wide d blocks (PV)
-  // LDS row strides (bytes).  K rows are read 16 bytes per lane, 32 rows at a
-  // time: a stride of 4 banks mod 64 keeps 16 lanes on distinct banks.  V rows
-  // are read with ds_read_b64_tr_b16 (4 rows x 32 bytes per 16 lanes, two
-  // groups per cycle): a stride of 16 banks mod 64 keeps those disjoint.
-  static constexpr int KSTR = D * 2 + 16;
-  static constexpr int VSTR = 320;
+  static constexpr int ROWS = 32 * NW;  // packed rows per workgroup
+  static constexpr int BN = 64;         // keys per tile
+  static constexpr int KC = D / 16;     // 16-wide d steps (QK^T)
+  static constexpr int DB = D / 32;     // 32-wide d blocks (PV)
+  // A K or V tile is 64 unpadded rows of 2D bytes whose 16-byte chunks are
+  // XOR-swizzled per row (swk / swv).  Wave w copies the rows of keys
+  // w*KPW .. w*KPW+KPW-1, RPW rows (1 KiB) per copy instruction.
+  static constexpr int RBYTES = 2 * D;
+  static constexpr int CPR = RBYTES / 16;  // chunks per row
+  static constexpr int RPW = 64 / CPR;     // rows per copy instruction
+  static constexpr int KPW = BN / NW;      // keys per wave
+  static constexpr int WPW = KPW / RPW;    // copy instructions per wave per matrix
+  // pipeline depth: data LA tiles ahead, indices IA = 2 LA tiles ahead
+  static constexpr int LA = 2;
+  static constexpr int IA = 2 * LA;
+  static constexpr int NBUF = LA + 1;
+  static constexpr int NRING = 8;  // ring slots (power of two, > IA)
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + BN * KSTR;
-  static constexpr int POS_OFF = V_OFF + BN * VSTR;
-  static constexpr int BUF_BYTES = POS_OFF + BN * 4;
-  static constexpr int RED_OFF = 2 * BUF_BYTES;
+  static constexpr int V_OFF = BN * RBYTES;
+  static constexpr int BUF_BYTES = 2 * BN * RBYTES;
+  // ring slot: [0, 256) cache-row source value per key, [256, 512) position
+  static constexpr int RING_OFF = NBUF * BUF_BYTES;
+  static constexpr int RING_BYTES = 2 * BN * 4;
+  static constexpr int RED_OFF = RING_OFF + NRING * RING_BYTES;
   static constexpr int RED_BYTES = NW * 4 * 32 * 4;  // [wave][block in tile][head] f32
   static constexpr int MISC_OFF = RED_OFF + RED_BYTES;
   static constexpr int LDS_BYTES = MISC_OFF + 64;
-  // loaders: 8 threads per key; parts 0-3 move a quarter K row, 4-7 a quarter V row
-  static constexpr int PART_BYTES = D / 2;
-  static constexpr int PCH = PART_BYTES / 16;  // 16-byte chunks per thread (2 or 4)
-  static_assert(VSTR >= D * 2, "V row stride");
+  // copies one wave issues per tile step: two index copies, K and V rows
+  static constexpr int COPIES_IDX = 2;
+  static constexpr int COPIES_DATA = 2 * WPW;
+  static constexpr int COPIES_STEP = COPIES_IDX + COPIES_DATA;
+  static_assert(WPW >= 1 && WPW * RPW == KPW, "copy split");
+  static_assert(LA == 2, "the prologue's wait counts assume two data tiles ahead");
+  static_assert(NRING > IA && (NRING & (NRING - 1)) == 0, "ring size");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
+
+// Chunk swizzles.  K fragments are read 16 rows x one 16-byte chunk per 16
+// lanes; V^T fragments by ds_read_b64_tr_b16, 4 rows x two chunks per 16
+// lanes, two such groups per cycle.  The XOR patterns put each of those
+// access sets on distinct banks.
+template <int D>
+__device__ inline int swk(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ inline int swv(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
 
 constexpr int kPosInvalid = 0x7fffffff;
 constexpr float kNegBig = -1.0e30f;
@@ -81,10 +103,6 @@ constexpr float kNegBig = -1.0e30f;
 struct Seg {
   int s, q0, n, c;
 };
-
-__device__ inline int key_position(const AttnArgs& a, const Seg& sg, int u) {
-  return u < sg.c ? u : a.positions[sg.q0 + u - sg.c];
-}
 
 // First virtual key index u in [0, c + n) whose position is >= target.
 // Positions are increasing in u and pos(u) >= u.  Wave-cooperative 64-ary
@@ -116,95 +134,139 @@ __device__ inline int first_key_at_or_after(const AttnArgs& a, const Seg& sg, in
 }
 
 // ----------------------------------------------------------------------------
-// tile pipeline: indices -> registers -> LDS
+// direct global -> LDS copies and the waits around them
 // ----------------------------------------------------------------------------
-// Thread t stages key t/8 of the tile: parts 0-3 a quarter of its K row,
-// parts 4-7 a quarter of its V row.  Keys past the visible range are clamped
-// to the last visible one (real, finite data) and get position INT_MAX so the
-// mask removes them; no branch depends on per-key data.
-template <class C, bool kWithV>
-struct Pipe {
-  int row;    // cache row (page * Hkv + g) * 16 + offset
-  int ipos;   // key position from the index stage
-  int dpos;   // the same, latched with the data stage
-  u32x4 d0, d1, d2, d3;  // staged data (d2, d3 unused when D = 64)
+// The copies are issued from inline assembly, so the compiler neither counts
+// them nor guards LDS reads against them: every wait below is explicit.
+// Loads of one wave complete in issue order, so "at most N outstanding"
+// means every copy but the last N issued has landed.  LDS base in M0 (one
+// wait state before the copy reads it); lane i's bytes land at base + i*size.
+// The base is the same in every lane of the wave.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lchar*)p;
+}
+__device__ __forceinline__ void copy16(uintptr_t src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+__device__ __forceinline__ void copy4(uintptr_t src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+// this wave's outstanding global loads (copies included) <= N
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// workgroup barrier that orders LDS only (no wait for outstanding copies)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
-  __device__ inline void index(const AttnArgs& a, const Seg& sg, int g, int u0, int u_end) {
-    const int kk = threadIdx.x >> 3;
-    const int u = u0 + kk;
+// ----------------------------------------------------------------------------
+// tile staging
+// ----------------------------------------------------------------------------
+// Keys past the visible range are clamped to the last visible one (real,
+// finite data) and get position INT_MAX, so the mask removes them; every
+// copy reads inside its array and no branch depends on per-key data.
+template <class C>
+struct Stager {
+  const AttnArgs& a;
+  const Seg& sg;
+  int g, t0, u_end, w, lane;
+  char* lds;
+  uint32_t l0;
+
+  __device__ inline int buf_off(int k) const { return (k % C::NBUF) * C::BUF_BYTES; }
+  __device__ inline int ring_off(int k) const {
+    return C::RING_OFF + (k & (C::NRING - 1)) * C::RING_BYTES;
+  }
+
+  // tile k, keys w*KPW + lane (lane < KPW): the page-table entry (cached key)
+  // or slot (own key) and the key's position, into ring slot k
+  __device__ inline void index(int k) const {
+    const int u = t0 + k * C::BN + w * C::KPW + lane;
     const int uu = min(u, u_end - 1);
     const bool cached = uu < sg.c;
     const int own = max(uu - sg.c, 0);
-    // select the index address arithmetically (a select of two kernel-argument
-    // pointers would be turned into a per-lane load of the argument itself)
+    // the source is selected arithmetically (a select of two kernel-argument
+    // pointers becomes a per-lane load of the argument)
     const uintptr_t bt = (uintptr_t)(a.block_table + (long)sg.s * a.max_pages + (uu >> 4));
     const uintptr_t sm = (uintptr_t)(a.slot_mapping + sg.q0 + own);
-    const int val = *(gint*)(cached ? bt : sm);
-    const int page = cached ? val : (val >> 4);
-    const int off = cached ? (uu & 15) : (val & 15);
-    row = (page * a.Hkv + g) * kPageSize + off;
-    const int opos = a.positions[sg.q0 + min(own, sg.n - 1)];
-    ipos = u < u_end ? (cached ? uu : opos) : kPosInvalid;
-  }
-
-  // Loads and stores are unconditional (a K-only sweep moves V too, unused),
-  // so the staged registers never live across divergent control flow.
-  __device__ inline void load(const AttnArgs& a) {
-    const int part = threadIdx.x & 7;
-    dpos = ipos;
-    const uintptr_t kb = (uintptr_t)a.k_cache, vb = (uintptr_t)a.v_cache;
-    const uintptr_t base = kb + (uintptr_t)(part >> 2) * (vb - kb);
-    gu32x4* src = (gu32x4*)(base + ((long)row * C::D + (part & 3) * (C::PART_BYTES / 2)) * 2);
-    d0 = src[0];
-    d1 = src[1];
-    if constexpr (C::PCH == 4) {
-      d2 = src[2];
-      d3 = src[3];
+    const uintptr_t ps = (uintptr_t)(a.positions + sg.q0 + min(own, sg.n - 1));
+    const uint32_t dst = l0 + ring_off(k) + w * C::KPW * 4;
+    if (lane < C::KPW) {
+      copy4(cached ? bt : sm, dst);
+      copy4(ps, dst + C::BN * 4);
     }
   }
 
-  __device__ inline void store(char* buf) const {
-    const int kk = threadIdx.x >> 3, part = threadIdx.x & 7;
-    char* dst = part < 4 ? buf + C::K_OFF + kk * C::KSTR + part * C::PART_BYTES
-                         : buf + C::V_OFF + kk * C::VSTR + (part - 4) * C::PART_BYTES;
-    ((u32x4*)dst)[0] = d0;
-    ((u32x4*)dst)[1] = d1;
-    if constexpr (C::PCH == 4) {
-      ((u32x4*)dst)[2] = d2;
-      ((u32x4*)dst)[3] = d3;
+  // tile k: K and V rows of this wave's keys into buffer k % NBUF, chunk
+  // (i % CPR) ^ sw(r) of row r to LDS chunk slot i % CPR; then the ring's
+  // position entries of these keys are finalised (cached key: u; past the
+  // visible range: INT_MAX)
+  __device__ inline void data(int k) const {
+    const int u0 = t0 + k * C::BN;
+    const int* rv = (const int*)(lds + ring_off(k));
+    int* rp = (int*)(lds + ring_off(k) + C::BN * 4);
+    const uint32_t dst = l0 + buf_off(k);
+#pragma unroll
+    for (int x = 0; x < C::WPW; ++x) {
+      const int rbase = w * C::KPW + x * C::RPW;
+      const int r = rbase + lane / C::CPR;
+      const int u = u0 + r;
+      const int uu = min(u, u_end - 1);
+      const bool cached = uu < sg.c;
+      const int val = rv[r];
+      const int page = cached ? val : (val >> 4);
+      const int off = cached ? (uu & 15) : (val & 15);
+      const long rowb = (long)((page * a.Hkv + g) * kPageSize + off) * C::RBYTES;
+      const int pc = lane % C::CPR;
+      copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,
+             dst + C::K_OFF + rbase * C::RBYTES);
+      copy16((uintptr_t)a.v_cache + rowb + (pc ^ swv<C::D>(r)) * 16,
+             dst + C::V_OFF + rbase * C::RBYTES);
+      if (pc == 0) rp[r] = u < u_end ? (cached ? uu : rp[r]) : kPosInvalid;
     }
-    if (part == 0) ((int*)(buf + C::POS_OFF))[kk] = dpos;
   }
 };
 
-// Runs body(buf, u0) over the key tiles [t0, u_end) in steps of 64 with the
-// index/data/LDS pipeline.  Every thread of the workgroup must call it.
-template <class C, bool kWithV, class Body>
+// Runs body(buf, kpos, u0) over the key tiles [t0, u_end) in steps of 64;
+// buf holds the tile's K and V, kpos its 64 key positions.  Every thread of
+// the workgroup must call it.  Pipeline, tile step t: index copies of tile
+// t+4, data copies of tile t+2, body(t), wait until this wave's copies of
+// tile t+1 have landed, barrier.  Copies past the last tile are clamped and
+// unused.
+template <class C, class Body>
 __device__ inline void sweep(const AttnArgs& a, const Seg& sg, int g, int t0, int u_end,
                              char* lds, Body&& body) {
   const int nt = (u_end - t0 + C::BN - 1) / C::BN;
   if (nt <= 0) return;
-  Pipe<C, kWithV> p;
-  p.index(a, sg, g, t0, u_end);
-  p.load(a);
-  if (nt > 1) p.index(a, sg, g, t0 + C::BN, u_end);
-  __syncthreads();  // the previous user of the buffers is done
-  p.store(lds);
-  __syncthreads();
-  if (nt > 1) {
-    p.load(a);
-    if (nt > 2) p.index(a, sg, g, t0 + 2 * C::BN, u_end);
-  }
+  const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                     (int)(threadIdx.x & 63), lds, lds_addr(lds)};
+  lds_barrier();  // the previous users of the buffers and the ring are done
+#pragma unroll
+  for (int k = 0; k < C::IA; ++k) st.index(k);
+  wait_loads<0>();
+  lds_barrier();
+#pragma unroll
+  for (int k = 0; k < C::LA; ++k) st.data(k);
+  wait_loads<C::COPIES_DATA>();  // tile 0 has landed
+  lds_barrier();
   for (int t = 0; t < nt; ++t) {
-    char* buf = lds + (t & 1) * C::BUF_BYTES;
-    body((const char*)buf, t0 + t * C::BN);
-    if (t + 1 < nt) p.store(lds + ((t + 1) & 1) * C::BUF_BYTES);
-    __syncthreads();
-    if (t + 2 < nt) {
-      p.load(a);
-      if (t + 3 < nt) p.index(a, sg, g, t0 + (t + 3) * C::BN, u_end);
-    }
+    st.index(t + C::IA);
+    st.data(t + C::LA);
+    body((const char*)(lds + st.buf_off(t)), (const int*)(lds + st.ring_off(t) + C::BN * 4),
+         t0 + t * C::BN);
+    wait_loads<C::COPIES_STEP>();  // everything but this step's copies: tile t+1
+    lds_barrier();
   }
+  wait_loads<0>();
 }
 
 // ----------------------------------------------------------------------------
@@ -262,18 +324,17 @@ __device__ inline void qk_tile(const char* buf, const bf16x8 (&qf)[C::KC], f32x1
   for (int kc = 0; kc < C::KC; ++kc) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 kf =
-          *(const bf16x8*)(buf + C::K_OFF + (mb * 32 + kr) * C::KSTR + (kc * 16 + h * 8) * 2);
+      const int R = mb * 32 + kr;
+      const bf16x8 kf = *(const bf16x8*)(buf + C::K_OFF + R * C::RBYTES +
+                                         (((kc * 2 + h) ^ swk<C::D>(R)) << 4));
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[mb], 0, 0, 0);
     }
   }
 }
 
 // Visibility mask of this lane's 32 keys for its row.
-template <class C>
-__device__ inline void apply_mask(const char* buf, int qpos, int window, f32x16 (&s)[2]) {
+__device__ inline void apply_mask(const int* kp, int qpos, int window, f32x16 (&s)[2]) {
   const int l = threadIdx.x & 63, h = l >> 5;
-  const int* kp = (const int*)(buf + C::POS_OFF);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -360,12 +421,13 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float ms = kNegBig, lsum = 0.f;  // running max (log2 units) and partial row sum
 
-  sweep<C, true>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds, [&](const char* buf, int u0) {
+  sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
+           [&](const char* buf, const int* kpos, int u0) {
     f32x16 sacc[2];
     qk_tile<C>(buf, qf, sacc);
-    const int kpos0 = ((const int*)(buf + C::POS_OFF))[0];
-    const bool full = (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos0 > pos_last - window);
-    if (!full) apply_mask<C>(buf, qpos, window, sacc);
+    const bool full =
+        (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
+    if (!full) apply_mask(kpos, qpos, window, sacc);
     const float mx = scaled_row_max(sacc, sl2);
     if (__any(mx > ms + kLazy)) {
       const float mnew = fmaxf(ms, mx);
@@ -377,31 +439,38 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       ms = mnew;
     }
-    float rs = 0.f;
     bf16x8 pf[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -ms));
-        rs += pv;
-        pf[mb * 2 + (e >> 3)][e & 7] = (__bf16)pv;
-      }
-    lsum += rs;
-    // O^T += V^T P^T; 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2.
-    // V^T fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 + 0..3 and
-    // ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which lane
-    // 4a+b of each 16-lane group points at V[key0 + a][d0 + 4b].
+      for (int e = 0; e < 16; ++e)
+        pf[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -ms));
+    // row sum of the bf16 probabilities the PV product uses, two per dot2
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][0], pf[ks][1]}, one2, rs0, false);
+      rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2], pf[ks][3]}, one2, rs1, false);
+      rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][4], pf[ks][5]}, one2, rs0, false);
+      rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, rs1, false);
+    }
+    lsum += rs0 + rs1;
+    // O^T += V^T P^T; 16-key step ks uses S^T registers (ks%2)*8.. of half
+    // ks/2.  V^T fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 +
+    // 0..3 and ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which
+    // lane 4a+b of each 16-lane group points at V[key0 + a][d0 + 4b].
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const char* vp = buf + C::V_OFF + (ks * 16 + h * 4 + ((l & 15) >> 2)) * C::VSTR +
-                         (db * 32 + (l & 16) + 4 * (l & 3)) * 2;
+        const int R = ks * 16 + h * 4 + ((l & 15) >> 2);
+        const int cv = db * 4 + ((l & 16) >> 3) + ((l & 3) >> 1);
+        const char* vp = buf + C::V_OFF + R * C::RBYTES + ((cv ^ swv<C::D>(R)) << 4) + 8 * (l & 1);
         const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (__attribute__((address_space(3))) bf16x4*)(vp));
         const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(vp + 8 * C::VSTR));
+            (__attribute__((address_space(3))) bf16x4*)(vp + 8 * C::RBYTES));
         const bf16x8 vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
@@ -462,10 +531,11 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     const int u_lo = window_start(a, sg, a.positions[sg.q0 + i_first], lds, C::MISC_OFF);
     // sweep 1: row max and normaliser over all visible keys
     float m = kNegBig, lsum = 0.f;
-    sweep<C, false>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds, [&](const char* buf, int u0) {
+    sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
+             [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
       qk_tile<C>(buf, qf, sacc);
-      apply_mask<C>(buf, qpos, window, sacc);
+      apply_mask(kpos, qpos, window, sacc);
       float mx = kNegBig;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -490,10 +560,11 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     const int first_pass = ps == passes - 1;
     int mt0 = 0;
     if (!first_pass && u_lo > sg.c) mt0 = (u_lo - sg.c) / C::BN;
-    sweep<C, false>(a, sg, g, sg.c + mt0 * C::BN, u_end, lds, [&](const char* buf, int u0) {
+    sweep<C>(a, sg, g, sg.c + mt0 * C::BN, u_end, lds,
+             [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
       qk_tile<C>(buf, qf, sacc);
-      apply_mask<C>(buf, qpos, window, sacc);
+      apply_mask(kpos, qpos, window, sacc);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -518,7 +589,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) red[(w * 4 + b) * 32 + l] = part[b];
       }
-      __syncthreads();
+      lds_barrier();
       if (tid < nbt * G) {
         const int bt = tid / G, h2 = tid % G;
         float tot = 0.f;
