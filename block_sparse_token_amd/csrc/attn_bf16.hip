@@ -62,7 +62,9 @@ struct Cfg {
   // pipeline depth: data LA tiles ahead, indices IA = 2 LA tiles ahead
   static constexpr int LA = 2;
   static constexpr int IA = 2 * LA;
-  static constexpr int NBUF = LA + 1;
+  // tile t is read in steps t and t+1 (waves 4-7 finish it a step late) and
+  // tiles t+1, t+2 are landing: four buffers
+  static constexpr int NBUF = 4;
   static constexpr int NRING = 8;  // ring slots (power of two, > IA)
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = BN * RBYTES;
@@ -81,6 +83,7 @@ struct Cfg {
   static_assert(WPW >= 1 && WPW * RPW == KPW, "copy split");
   static_assert(LA == 2, "the prologue's wait counts assume two data tiles ahead");
   static_assert(NRING > IA && (NRING & (NRING - 1)) == 0, "ring size");
+  static_assert(NBUF == 4, "buffer rotation");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -182,7 +185,7 @@ struct Stager {
   char* lds;
   uint32_t l0;
 
-  __device__ inline int buf_off(int k) const { return (k % C::NBUF) * C::BUF_BYTES; }
+  __device__ inline int buf_off(int k) const { return (k & (C::NBUF - 1)) * C::BUF_BYTES; }
   __device__ inline int ring_off(int k) const {
     return C::RING_OFF + (k & (C::NRING - 1)) * C::RING_BYTES;
   }
@@ -225,7 +228,8 @@ struct Stager {
       const int val = rv[r];
       const int page = cached ? val : (val >> 4);
       const int off = cached ? (uu & 15) : (val & 15);
-      const long rowb = (long)((page * a.Hkv + g) * kPageSize + off) * C::RBYTES;
+      // page < 2^24 and Hkv < 2^8 (checked by the host)
+      const long rowb = (long)((__umul24(page, a.Hkv) + g) * kPageSize + off) * C::RBYTES;
       const int pc = lane % C::CPR;
       copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,
              dst + C::K_OFF + rbase * C::RBYTES);
@@ -236,19 +240,13 @@ struct Stager {
   }
 };
 
-// Runs body(buf, kpos, u0) over the key tiles [t0, u_end) in steps of 64;
-// buf holds the tile's K and V, kpos its 64 key positions.  Every thread of
-// the workgroup must call it.  Pipeline, tile step t: index copies of tile
-// t+4, data copies of tile t+2, body(t), wait until this wave's copies of
-// tile t+1 have landed, barrier.  Copies past the last tile are clamped and
-// unused.
-template <class C, class Body>
-__device__ inline void sweep(const AttnArgs& a, const Seg& sg, int g, int t0, int u_end,
-                             char* lds, Body&& body) {
-  const int nt = (u_end - t0 + C::BN - 1) / C::BN;
-  if (nt <= 0) return;
-  const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
-                     (int)(threadIdx.x & 63), lds, lds_addr(lds)};
+// Pipeline over the key tiles [t0, u_end) in steps of 64.  Tile step t:
+// index copies of tile t+4, data copies of tile t+2, the step's work on tile
+// t (and t-1), wait until this wave's copies of tile t+1 have landed,
+// barrier.  Copies past the last tile are clamped and unused.  Every thread
+// of the workgroup runs the same steps.
+template <class C>
+__device__ inline void sweep_prologue(const Stager<C>& st) {
   lds_barrier();  // the previous users of the buffers and the ring are done
 #pragma unroll
   for (int k = 0; k < C::IA; ++k) st.index(k);
@@ -258,13 +256,33 @@ __device__ inline void sweep(const AttnArgs& a, const Seg& sg, int g, int t0, in
   for (int k = 0; k < C::LA; ++k) st.data(k);
   wait_loads<C::COPIES_DATA>();  // tile 0 has landed
   lds_barrier();
+}
+template <class C>
+__device__ inline void sweep_issue(const Stager<C>& st, int t) {
+  st.index(t + C::IA);
+  st.data(t + C::LA);
+}
+template <class C>
+__device__ inline void sweep_step_end() {
+  wait_loads<C::COPIES_STEP>();  // everything but this step's copies: tile t+1
+  lds_barrier();
+}
+
+// Runs body(buf, kpos, u0) over the tiles; buf holds the tile's K and V,
+// kpos its 64 key positions.
+template <class C, class Body>
+__device__ inline void sweep(const AttnArgs& a, const Seg& sg, int g, int t0, int u_end,
+                             char* lds, Body&& body) {
+  const int nt = (u_end - t0 + C::BN - 1) / C::BN;
+  if (nt <= 0) return;
+  const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                     (int)(threadIdx.x & 63), lds, lds_addr(lds)};
+  sweep_prologue(st);
   for (int t = 0; t < nt; ++t) {
-    st.index(t + C::IA);
-    st.data(t + C::LA);
+    sweep_issue(st, t);
     body((const char*)(lds + st.buf_off(t)), (const int*)(lds + st.ring_off(t) + C::BN * 4),
          t0 + t * C::BN);
-    wait_loads<C::COPIES_STEP>();  // everything but this step's copies: tile t+1
-    lds_barrier();
+    sweep_step_end<C>();
   }
   wait_loads<0>();
 }
@@ -312,10 +330,54 @@ __device__ inline void load_q(const AttnArgs& a, long qrow_elem, bool valid, int
     for (int e = 0; e < 8; ++e) qf[kc][e] = (__bf16)x[kc][e];
 }
 
+// LDS fragment addresses.  Per lane, the byte offset inside a tile buffer
+// of its K fragment for each 16-wide d step kc (key row kr = l%32, chunk
+// (2kc + h) ^ swk(kr)) and of its V^T transpose-read start for each 32-wide d
+// block db (row h*4 + (l%16)/4 of each 16-key step).  Neither swizzle
+// depends on the 32-key half, the 16-key step or the upper 8 keys of a
+// step, so those stay immediate offsets of the reads.
+typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
+template <class C>
+struct FragOffsets {
+  uint32_t k[C::KC], v[C::DB];
+  __device__ inline FragOffsets() {
+    const int l = threadIdx.x & 63, h = l >> 5, kr = l & 31;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+      k[kc] = C::K_OFF + kr * C::RBYTES + (((kc * 2 + h) ^ swk<C::D>(kr)) << 4);
+    const int R = h * 4 + ((l & 15) >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int cv = db * 4 + ((l & 16) >> 3) + ((l & 3) >> 1);
+      v[db] = C::V_OFF + R * C::RBYTES + ((cv ^ swv<C::D>(R)) << 4) + 8 * (l & 1);
+    }
+  }
+};
+// A tile's fragment addresses: the offsets plus the buffer's LDS address.
+// The empty asm keeps each sum in one register, so the compiler folds the
+// constant parts into the reads instead of keeping one register per read.
+template <class C>
+struct TileFrag {
+  uint32_t k[C::KC], v[C::DB];
+  __device__ inline TileFrag(const FragOffsets<C>& f, uint32_t base) {
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+      k[kc] = f.k[kc] + base;
+      asm("" : "+v"(k[kc]));
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      v[db] = f.v[db] + base;
+      asm("" : "+v"(v[db]));
+    }
+  }
+};
+
 // S^T = K Q^T for one 64-key tile: s[mb], mb = 32-key half of the tile
 template <class C>
-__device__ inline void qk_tile(const char* buf, const bf16x8 (&qf)[C::KC], f32x16 (&s)[2]) {
-  const int l = threadIdx.x & 63, h = l >> 5, kr = l & 31;
+__device__ inline void qk_tile(const TileFrag<C>& tf, const bf16x8 (&qf)[C::KC],
+                               f32x16 (&s)[2]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -324,9 +386,7 @@ __device__ inline void qk_tile(const char* buf, const bf16x8 (&qf)[C::KC], f32x1
   for (int kc = 0; kc < C::KC; ++kc) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const int R = mb * 32 + kr;
-      const bf16x8 kf = *(const bf16x8*)(buf + C::K_OFF + R * C::RBYTES +
-                                         (((kc * 2 + h) ^ swk<C::D>(R)) << 4));
+      const bf16x8 kf = *(lbf16x8*)(uintptr_t)(tf.k[kc] + mb * 32 * C::RBYTES);
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s[mb], 0, 0, 0);
     }
   }
@@ -351,7 +411,18 @@ __device__ inline void apply_mask(const int* kp, int qpos, int window, f32x16 (&
   }
 }
 
-__device__ inline float pair_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
+// Reductions over the lane pair (l, l^32): v_permlane32_swap of x with
+// itself leaves x(l % 32) in one result and x(l % 32 + 32) in the other.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline int window_start(const AttnArgs& a, const Seg& sg, int pos_first, char* lds,
                                    int misc_off) {
@@ -420,14 +491,28 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   float ms = kNegBig, lsum = 0.f;  // running max (log2 units) and partial row sum
+  f32x16 sacc[2];                  // S^T of the tile between QK and softmax
 
-  sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
-           [&](const char* buf, const int* kpos, int u0) {
-    f32x16 sacc[2];
-    qk_tile<C>(buf, qf, sacc);
+  const int t0 = (u_lo / C::BN) * C::BN;
+  const int nt = (u_end - t0 + C::BN - 1) / C::BN;
+  const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(w),
+                     l, lds, lds_addr(lds)};
+
+  // S^T of tile t, masked where the tile is not entirely visible
+  const FragOffsets<C> fo;
+  const uint32_t l0 = lds_addr(lds);
+  auto qk = [&](int t) {
+    const TileFrag<C> tf(fo, l0 + st.buf_off(t));
+    const int* kpos = (const int*)(lds + st.ring_off(t) + C::BN * 4);
+    qk_tile<C>(tf, qf, sacc);
+    const int u0 = t0 + t * C::BN;
     const bool full =
         (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
     if (!full) apply_mask(kpos, qpos, window, sacc);
+  };
+  // softmax of S^T (tile t) and O^T += V^T P^T
+  auto softmax_pv = [&](int t) {
+    const TileFrag<C> tf(fo, l0 + st.buf_off(t));
     const float mx = scaled_row_max(sacc, sl2);
     if (__any(mx > ms + kLazy)) {
       const float mnew = fmaxf(ms, mx);
@@ -456,29 +541,48 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, rs1, false);
     }
     lsum += rs0 + rs1;
-    // O^T += V^T P^T; 16-key step ks uses S^T registers (ks%2)*8.. of half
-    // ks/2.  V^T fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 +
-    // 0..3 and ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which
-    // lane 4a+b of each 16-lane group points at V[key0 + a][d0 + 4b].
+    // 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2.  V^T
+    // fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 + 0..3 and
+    // ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which lane
+    // 4a+b of each 16-lane group points at V[key0 + a][d0 + 4b].
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
-        const int R = ks * 16 + h * 4 + ((l & 15) >> 2);
-        const int cv = db * 4 + ((l & 16) >> 3) + ((l & 3) >> 1);
-        const char* vp = buf + C::V_OFF + R * C::RBYTES + ((cv ^ swv<C::D>(R)) << 4) + 8 * (l & 1);
-        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(vp));
-        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) bf16x4*)(vp + 8 * C::RBYTES));
+        const uint32_t vp = tf.v[db] + ks * 16 * C::RBYTES;
+        const bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4*)(uintptr_t)vp);
+        const bf16x4 hi4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4*)(uintptr_t)(vp + 8 * C::RBYTES));
         const bf16x8 vf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
     }
-  });
+  };
+
+  // The two waves that share a SIMD (w and w+4) work on different stages:
+  // waves 0-3 run QK, softmax and PV of tile t in step t; waves 4-7 run
+  // softmax and PV of tile t-1, then QK of tile t.  While one issues matrix
+  // instructions the other mostly runs the vector softmax.  One extra step
+  // lets waves 4-7 finish the last tile.
+  const bool lead = w < C::NW / 2;
+  sweep_prologue(st);
+  for (int t = 0; t <= nt; ++t) {
+    sweep_issue(st, t);
+    if (lead) {
+      if (t < nt) {
+        qk(t);
+        softmax_pv(t);
+      }
+    } else {
+      if (t > 0) softmax_pv(t - 1);
+      if (t < nt) qk(t);
+    }
+    sweep_step_end<C>();
+  }
+  wait_loads<0>();
 
   // epilogue: normalise and store; lane holds d = db*32 + jg*8 + h*4 + e
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float ltot = pair_sum(lsum);
   if (!rvalid) return;
   uint16_t* out = (uint16_t*)a.out;
   const float inv = 1.f / ltot;
@@ -515,6 +619,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
   const int window = a.window;
   float* red = (float*)(lds + C::RED_OFF);
   const int nbt = B >= 64 ? 1 : 64 / B;  // blocks per 64-key tile
+  const FragOffsets<C> fo;
 
   for (int ps = passes - 1; ps >= 0; --ps) {
     const int rbeg = ps * C::ROWS;
@@ -534,7 +639,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
              [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
-      qk_tile<C>(buf, qf, sacc);
+      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
       apply_mask(kpos, qpos, window, sacc);
       float mx = kNegBig;
 #pragma unroll
@@ -552,7 +657,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
         for (int e = 0; e < 16; ++e) rs += __builtin_amdgcn_exp2f(sacc[mb][e] * sl2 - mnew * sl2);
       lsum = lsum * alpha + rs;
     });
-    const float lt = lsum + __shfl_xor(lsum, 32, 64);
+    const float lt = pair_sum(lsum);
     const float inv = rvalid ? 1.f / lt : 0.f;
     const float mb2 = m * sl2;
     // sweep 2: own keys in 64-key tiles from the segment start.  The first
@@ -563,7 +668,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     sweep<C>(a, sg, g, sg.c + mt0 * C::BN, u_end, lds,
              [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
-      qk_tile<C>(buf, qf, sacc);
+      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
       apply_mask(kpos, qpos, window, sacc);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -581,7 +686,7 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         float x = part[b];
-        x += __shfl_xor(x, 32, 64);
+        x = pair_sum(x);
         for (int o = 16; o >= G; o >>= 1) x += __shfl_xor(x, o, 64);
         part[b] = x;
       }
