@@ -567,14 +567,15 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const bool lead = w < C::NW / 2;
   sweep_prologue(st);
   for (int t = 0; t <= nt; ++t) {
-    sweep_issue(st, t);
+    // the two waves of a SIMD issue their copies at different points of the
+    // step, so the copies of a step never all queue at once
     if (lead) {
-      if (t < nt) {
-        qk(t);
-        softmax_pv(t);
-      }
+      if (t < nt) qk(t);
+      sweep_issue(st, t);
+      if (t < nt) softmax_pv(t);
     } else {
       if (t > 0) softmax_pv(t - 1);
+      sweep_issue(st, t);
       if (t < nt) qk(t);
     }
     sweep_step_end<C>();
