@@ -575,8 +575,8 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       if (t < nt) softmax_pv(t);
     } else {
       if (t > 0) softmax_pv(t - 1);
-      sweep_issue(st, t);
       if (t < nt) qk(t);
+      sweep_issue(st, t);
     }
     sweep_step_end<C>();
   }
