@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
-WORKLOAD = "c2"
+WORKLOAD = "packed_llama8b"
 
 
 def parse():

@@ -108,6 +108,7 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   const int G = Hq / Hkv;
   if (G > 32 || (G & (G - 1)))
     return fail(UP_ERR_UNSUPPORTED, "Hq / Hkv must be a power of two <= 32 (got %d)", G);
+  if (Hkv > 255) return fail(UP_ERR_UNSUPPORTED, "at most 255 KV heads (got %d)", Hkv);
   if (D != 64 && D != 128) return fail(UP_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", D);
   if (!q || !k || !v || !k_cache || !v_cache || !out)
     return fail(UP_ERR_INVALID, "q, k, v, k_cache, v_cache and out must be non-NULL");

@@ -228,7 +228,8 @@ struct Stager {
       const int val = rv[r];
       const int page = cached ? val : (val >> 4);
       const int off = cached ? (uu & 15) : (val & 15);
-      // page < 2^24 and Hkv < 2^8 (checked by the host)
+      // 24-bit product: Hkv <= 255 (checked by the host), page * Hkv < 2^27
+      // (a documented precondition on the cache size)
       const long rowb = (long)((__umul24(page, a.Hkv) + g) * kPageSize + off) * C::RBYTES;
       const int pc = lane % C::CPR;
       copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,

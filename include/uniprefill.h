@@ -40,8 +40,9 @@
  *  - Device-side preconditions are the caller's: cu_seqlens non-decreasing
  *    with every segment holding >= 1 token, cu_seqlens[S] <= T, positions
  *    strictly increasing inside a segment and >= that segment's ctx_len,
- *    page ids in [0, num_pages), slots in range, cu_blocks consistent with
- *    cu_seqlens and block_size.
+ *    page ids in [0, num_pages), num_pages * Hkv < 2^27 (cache rows are
+ *    addressed with 32-bit indices), slots in range, cu_blocks consistent
+ *    with cu_seqlens and block_size.
  *  - The library is thread-safe; its only global state is the thread-local
  *    error text.
  */

@@ -39,22 +39,22 @@ def _check_segments(wl, call, g, cached_of, score_segs, rng, k_rows=6):
     H.check_selection_and_compaction(wl, call, g)
 
 
-def test_gpu_c2_full():
+def test_gpu_packed_llama8b_full():
     import gpu_harness as H
-    wl = W.make("c2")
+    wl = W.make("packed_llama8b")
     call = wl.calls[0]
-    H.log(f"c2: T={call.T}")
+    H.log(f"packed_llama8b: T={call.T}")
     kc, vc = H.make_caches(wl)
     g = H.gpu_result(H.launch_call(wl, call, kc, vc))
-    H.log("c2: gpu done, checking")
+    H.log("packed_llama8b: gpu done, checking")
     _check_segments(wl, call, g, lambda si, s: None, set(range(len(call.segments))),
                     np.random.default_rng(0))
-    H.log("c2: ok")
+    H.log("packed_llama8b: ok")
 
 
-def test_gpu_c3_full_chunked():
+def test_gpu_chunked_128k_full():
     import gpu_harness as H
-    wl = W.make("c3")
+    wl = W.make("chunked_128k")
     kc, vc = H.make_caches(wl)
     rng = np.random.default_rng(1)
     check = {0, 1, 7, 15}
@@ -64,7 +64,7 @@ def test_gpu_c3_full_chunked():
             # selection and compaction are checked bit-exact for every call
             H.check_selection_and_compaction(wl, call, g)
             continue
-        H.log(f"c3: call {ci} ctx={call.segments[0].ctx}")
+        H.log(f"chunked_128k: call {ci} ctx={call.segments[0].ctx}")
 
         def cached_of(si, s, ci=ci):
             if s.ctx == 0:
@@ -73,17 +73,17 @@ def test_gpu_c3_full_chunked():
             return oracle.apply_rope(kk, pp, wl.theta), vv
 
         _check_segments(wl, call, g, cached_of, {0}, rng, k_rows=4)
-    H.log("c3: ok")
+    H.log("chunked_128k: ok")
 
 
-def test_gpu_c4_full_mixed_step():
+def test_gpu_mixed_decode_prefill_full():
     import gpu_harness as H
-    wl = W.make("c4")
+    wl = W.make("mixed_decode_prefill")
     call = wl.calls[0]
-    H.log(f"c4: T={call.T} segments={len(call.segments)}")
+    H.log(f"mixed_decode_prefill: T={call.T} segments={len(call.segments)}")
     kc, vc = H.make_caches(wl)
     g = H.gpu_result(H.launch_call(wl, call, kc, vc))
-    H.log("c4: gpu done")
+    H.log("mixed_decode_prefill: gpu done")
     n_dec = sum(1 for s in call.segments if not s.flagged)
     rng = np.random.default_rng(2)
     ctxs = [s.ctx for s in call.segments[:n_dec]]
@@ -104,19 +104,19 @@ def test_gpu_c4_full_mixed_step():
         H.check_scores("bf16", g["scores"][g["cu_blocks"][si]:g["cu_blocks"][si + 1]],
                        r["scores"])
     H.check_selection_and_compaction(wl, call, g)
-    H.log("c4: ok")
+    H.log("mixed_decode_prefill: ok")
 
 
-def test_gpu_c5_full_with_sliding_window_layer():
+def test_gpu_swa_after_selection_full():
     import gpu_harness as H
     from block_sparse_token_amd import step as ST
-    wl = W.make("c5")
+    wl = W.make("swa_after_selection")
     call = wl.calls[0]
-    H.log(f"c5: T={call.T}")
+    H.log(f"swa_after_selection: T={call.T}")
     kc, vc = H.make_caches(wl)
     pc = H.launch_call(wl, call, kc, vc)
     g = H.gpu_result(pc)
-    H.log("c5: layer 1 done")
+    H.log("swa_after_selection: layer 1 done")
     rng = np.random.default_rng(3)
     _check_segments(wl, call, g, lambda si, s: None, set(range(len(call.segments))), rng)
     # layer 2: sliding window over the kept tokens at their original positions,
@@ -135,7 +135,7 @@ def test_gpu_c5_full_with_sliding_window_layer():
     l2.launch()
     torch.cuda.synchronize()
     out2 = ST.tensor_to_stored(l2.out)
-    H.log(f"c5: layer 2 done on {nk} kept tokens")
+    H.log(f"swa_after_selection: layer 2 done on {nk} kept tokens")
     ro = g["rows_out"]
     cu2 = g["cu_seqlens_out"]
     for si in range(S):
@@ -145,4 +145,4 @@ def test_gpu_c5_full_with_sliding_window_layer():
                                    window=wl.layer2["window"], q=ro["q2"], k=ro["k2"],
                                    v=ro["v2"], positions=ro["positions"], cu=cu2)
         H.check_out("bf16", out2[cu2[si] + np.asarray(rows)], r["out"], f"layer2 segment {si}")
-    H.log("c5: ok")
+    H.log("swa_after_selection: ok")

@@ -41,12 +41,12 @@ def _run_and_check(wl, check_lse=True):
     return True
 
 
-def test_gpu_c1_chunked_fp32():
-    assert _run_and_check(W.make("c1"))
+def test_gpu_small_chunked_fp32():
+    assert _run_and_check(W.make("small_chunked_fp32"))
 
 
-def test_gpu_c1_second_seed_with_rope():
-    wl = W.make("c1", seed=101)
+def test_gpu_small_chunked_fp32_second_seed_with_rope():
+    wl = W.make("small_chunked_fp32", seed=101)
     wl.theta = 500000.0
     assert _run_and_check(wl)
 

@@ -268,10 +268,10 @@ def test_run_call_p_one_keeps_everything():
 
 
 # ---------------------------------------------------------------- whole workloads
-def test_c1_chunked_calls_equal_one_pass_per_prompt():
+def test_small_chunked_fp32_chunked_calls_equal_one_pass_per_prompt():
     import workloads as W
     from oracle import driver
-    wl = W.make("c1")
+    wl = W.make("small_chunked_fp32")
     res = driver.run_workload(wl, threads=1)
     # gather each prompt's outputs across calls, in position order
     got = {}

@@ -17,8 +17,8 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
 
 
-def test_c1_schedule():
-    wl = W.make("c1")
+def test_small_chunked_fp32_schedule():
+    wl = W.make("small_chunked_fp32")
     assert [c.T for c in wl.calls] == [229, 100, 64, 63]
     assert wl.calls[0].q.dtype == np.float32 and wl.calls[0].q.shape == (229, 2, 64)
     assert [(s.prompt, s.ctx, s.n) for s in wl.calls[1].segments] == [(1, 64, 36), (3, 64, 64)]
@@ -35,16 +35,16 @@ def test_c1_schedule():
 
 
 def test_deterministic():
-    a, b = W.make("c1"), W.make("c1")
+    a, b = W.make("small_chunked_fp32"), W.make("small_chunked_fp32")
     for ca, cb in zip(a.calls, b.calls):
         assert np.array_equal(ca.q, cb.q) and np.array_equal(ca.k, cb.k)
         assert np.array_equal(ca.slot_mapping, cb.slot_mapping)
-    c = W.make("c1", seed=101)
+    c = W.make("small_chunked_fp32", seed=101)
     assert not np.array_equal(a.calls[0].q, c.calls[0].q)
 
 
 def test_heavy_hitters_c1():
-    wl = W.make("c1")
+    wl = W.make("small_chunked_fp32")
     # 3 of the 30 groups carry +3u: their keys have a large common component
     ks = np.concatenate([c.k for c in wl.calls])  # packed order differs from prompt order,
     norms = np.linalg.norm(ks.astype(np.float64), axis=-1).mean(axis=1)
@@ -61,11 +61,11 @@ def test_custom_given_cache_and_paging():
         assert np.array_equal(kc[pg[pos // 16], :, pos % 16], K[pos])
 
 
-@pytest.mark.parametrize("name", ["c2", "c4"])
+@pytest.mark.parametrize("name", ["packed_llama8b", "mixed_decode_prefill"])
 def test_big_configs_shapes(name):
-    wl = W.make(name) if name != "c4" else W.make("c4", device_cache=True)
+    wl = W.make(name) if name != "mixed_decode_prefill" else W.make("mixed_decode_prefill", device_cache=True)
     c = wl.calls[0]
-    if name == "c2":
+    if name == "packed_llama8b":
         assert len(c.segments) == 16 and 16 * 512 <= c.T <= 16 * 8192
         assert c.q.shape == (c.T, 32, 128) and c.hidden.shape == (c.T, 4096)
     else:

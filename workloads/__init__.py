@@ -255,7 +255,7 @@ def _chunk_schedule(lengths, chunk, ctx0=None, flag=True):
     return calls
 
 
-def config_c1(seed: int = 1) -> Workload:
+def config_small_chunked_fp32(seed: int = 1) -> Workload:
     """Tiny packed prefill, fp32: 4 prompts {37,100,64,255}, 2+2 heads x 64,
     block 16, p 0.9, chunk 64 (so later chunks attend their cached KV)."""
     rng = np.random.default_rng(seed)
@@ -267,12 +267,12 @@ def config_c1(seed: int = 1) -> Workload:
     qs, ks, vs, hs = _pack_calls(sched, None, 2, 2, 64, 128, "f32", rng, 1.0, heavy, u)
     npages, pages = _pages_for(rng, plen)
     calls = _finish_calls(sched, qs, ks, vs, hs, pages)
-    return Workload(name="c1", dtype="f32", Hq=2, Hkv=2, D=64, block_size=16, p=0.9, theta=0.0,
+    return Workload(name="small_chunked_fp32", dtype="f32", Hq=2, Hkv=2, D=64, block_size=16, p=0.9, theta=0.0,
                     window=0, hidden_width=128, num_pages=npages, prompt_pages=pages,
                     prompt_len=plen, calls=calls, seed=seed)
 
 
-def config_c2(seed: int = 2) -> Workload:
+def config_packed_llama8b(seed: int = 2) -> Workload:
     """Llama-3.1-8B-shaped layer, bf16: 16 prompts U{512..8192} packed in one
     call, 32/8 heads x 128, q,k,v ~ N(0,1)/sqrt(128), rotary base 500000,
     block 64, p 0.95, hidden width 4096."""
@@ -286,12 +286,12 @@ def config_c2(seed: int = 2) -> Workload:
                                  heavy, u)
     npages, pages = _pages_for(rng, plen)
     calls = _finish_calls(sched, qs, ks, vs, hs, pages)
-    return Workload(name="c2", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.95,
+    return Workload(name="packed_llama8b", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.95,
                     theta=500000.0, window=0, hidden_width=4096, num_pages=npages,
                     prompt_pages=pages, prompt_len=plen, calls=calls, seed=seed)
 
 
-def config_c3(seed: int = 3, total: int = 131072, chunk: int = 8192) -> Workload:
+def config_chunked_128k(seed: int = 3, total: int = 131072, chunk: int = 8192) -> Workload:
     """One long prompt in chunks over a paged cache: 131072 tokens, chunk 8192,
     bf16, Llama-3.1-8B heads, block 128, p 0.9.  Heavy-hitter groups are 5% of
     the groups, one contiguous cluster from token 0."""
@@ -306,12 +306,12 @@ def config_c3(seed: int = 3, total: int = 131072, chunk: int = 8192) -> Workload
     qs, ks, vs, hs = _pack_calls(sched, None, 32, 8, 128, 4096, "bf16", rng, 1.0, heavy, u)
     npages, pages = _pages_for(rng, plen)
     calls = _finish_calls(sched, qs, ks, vs, hs, pages)
-    return Workload(name="c3", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=128, p=0.9,
+    return Workload(name="chunked_128k", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=128, p=0.9,
                     theta=500000.0, window=0, hidden_width=4096, num_pages=npages,
                     prompt_pages=pages, prompt_len=plen, calls=calls, seed=seed)
 
 
-def config_c4(seed: int = 4, n_decode: int = 256, budget: int = 8192,
+def config_mixed_decode_prefill(seed: int = 4, n_decode: int = 256, budget: int = 8192,
               ctx_range=(1024, 32768), wait_range=(4096, 65536), n_wait: int = 6,
               device_cache: bool = True) -> Workload:
     """Continuous-batching step: 256 decodes (1 token, cached context
@@ -340,7 +340,7 @@ def config_c4(seed: int = 4, n_decode: int = 256, budget: int = 8192,
     qs, ks, vs, hs = _pack_calls([segs], None, 32, 8, 128, 4096, "bf16", rng, 1.0, heavy, u)
     npages, pages = _pages_for(rng, plen)
     calls = _finish_calls([segs], qs, ks, vs, hs, pages)
-    wl = Workload(name="c4", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.95,
+    wl = Workload(name="mixed_decode_prefill", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.95,
                   theta=500000.0, window=0, hidden_width=4096, num_pages=npages,
                   prompt_pages=pages, prompt_len=plen, calls=calls, seed=seed)
     cache_seed = int(rng.integers(0, 2**31 - 1))
@@ -356,7 +356,7 @@ def config_c4(seed: int = 4, n_decode: int = 256, budget: int = 8192,
     return wl
 
 
-def config_c5(seed: int = 5, n_prompts: int = 8, len_range=(8192, 32768)) -> Workload:
+def config_swa_after_selection(seed: int = 5, n_prompts: int = 8, len_range=(8192, 32768)) -> Workload:
     """Hybrid-layer propagation: a full-attention layer scores and selects on 8
     prompts U{8192..32768} (block 64, p 0.9); compaction then carries hidden
     states, positions, slots and the second layer's q/k/v; a sliding-window
@@ -376,13 +376,13 @@ def config_c5(seed: int = 5, n_prompts: int = 8, len_range=(8192, 32768)) -> Wor
         "k2": _store(_normal32(rng, (T, 8, 128)), "bf16"),
         "v2": _store(_normal32(rng, (T, 8, 128)), "bf16"),
     }
-    return Workload(name="c5", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.9,
+    return Workload(name="swa_after_selection", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=64, p=0.9,
                     theta=500000.0, window=0, hidden_width=4096, num_pages=npages,
                     prompt_pages=pages, prompt_len=plen, calls=calls,
                     layer2={"window": 4096, "theta": 500000.0}, seed=seed)
 
 
-CONFIGS = {"c1": config_c1, "c2": config_c2, "c3": config_c3, "c4": config_c4, "c5": config_c5}
+CONFIGS = {"small_chunked_fp32": config_small_chunked_fp32, "packed_llama8b": config_packed_llama8b, "chunked_128k": config_chunked_128k, "mixed_decode_prefill": config_mixed_decode_prefill, "swa_after_selection": config_swa_after_selection}
 
 
 def make(name: str, seed: int | None = None, **kw) -> Workload:
