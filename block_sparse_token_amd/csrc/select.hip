@@ -148,20 +148,41 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __rest
       if ((key & mask) == prefix) atomicAdd(&hq[(key >> shift) & 255u], fx_score(sc[k]));
     }
     __syncthreads();
-    if (tid == 0) {
-      unsigned long long cum = 0;
-      const unsigned long long need = s_need;
-      int bstar = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hq[b] >= need) {
-          bstar = b;
-          break;
-        }
-        cum += hq[b];
+    // Highest bin b* with (mass of bins above b*) + hq[b*] >= need, and the
+    // mass above it.  Wave 0: lane i holds bins 255-4i .. 252-4i (descending),
+    // an exclusive scan over lanes gives each lane the mass above its bins,
+    // and the first lane (in bin order) whose bins reach the need decides.
+    if (tid < 64) {
+      const int lane = tid;
+      unsigned long long v[4], loc = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = hq[255 - 4 * lane - j];
+        loc += v[j];
       }
-      s_need = need - cum;
-      s_above += cum;
-      s_prefix = prefix | ((uint32_t)bstar << shift);
+      unsigned long long incl = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const unsigned long long need = s_need;
+      unsigned long long cum = incl - loc;  // mass of all bins above this lane's
+      int hit = -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (hit < 0 && cum + v[j] >= need) hit = j;
+        if (hit < 0) cum += v[j];
+      }
+      const unsigned long long found = __ballot(hit >= 0);
+      // no bin reaches the need: b* = 0 with every bin counted above it
+      const int first = found ? __ffsll((long long)found) - 1 : 63;
+      if (lane == first) {
+        const int bstar = hit >= 0 ? 255 - 4 * lane - hit : 0;
+        s_need = need - cum;
+        s_above += cum;
+        s_prefix = prefix | ((uint32_t)bstar << shift);
+      }
     }
     mask |= 255u << shift;
     __syncthreads();
