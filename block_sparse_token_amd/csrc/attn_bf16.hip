@@ -190,10 +190,11 @@ struct Stager {
     return C::RING_OFF + (k & (C::NRING - 1)) * C::RING_BYTES;
   }
 
-  // tile k, keys w*KPW + lane (lane < KPW): the page-table entry (cached key)
-  // or slot (own key) and the key's position, into ring slot k
+  // tile k: wave 0 brings, for key `lane`, the page-table entry (cached key)
+  // or slot (own key) and the key's position into ring slot k
   __device__ inline void index(int k) const {
-    const int u = t0 + k * C::BN + w * C::KPW + lane;
+    if (w != 0) return;
+    const int u = t0 + k * C::BN + lane;
     const int uu = min(u, u_end - 1);
     const bool cached = uu < sg.c;
     const int own = max(uu - sg.c, 0);
@@ -202,11 +203,9 @@ struct Stager {
     const uintptr_t bt = (uintptr_t)(a.block_table + (long)sg.s * a.max_pages + (uu >> 4));
     const uintptr_t sm = (uintptr_t)(a.slot_mapping + sg.q0 + own);
     const uintptr_t ps = (uintptr_t)(a.positions + sg.q0 + min(own, sg.n - 1));
-    const uint32_t dst = l0 + ring_off(k) + w * C::KPW * 4;
-    if (lane < C::KPW) {
-      copy4(cached ? bt : sm, dst);
-      copy4(ps, dst + C::BN * 4);
-    }
+    const uint32_t dst = l0 + ring_off(k);
+    copy4(cached ? bt : sm, dst);
+    copy4(ps, dst + C::BN * 4);
   }
 
   // tile k: K and V rows of this wave's keys into buffer k % NBUF, chunk
@@ -265,7 +264,10 @@ __device__ inline void sweep_issue(const Stager<C>& st, int t) {
 }
 template <class C>
 __device__ inline void sweep_step_end() {
-  wait_loads<C::COPIES_STEP>();  // everything but this step's copies: tile t+1
+  // everything but this step's copies (wave 0 also issued the index copies):
+  // tile t+1 has landed
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) wait_loads<C::COPIES_STEP>();
+  else wait_loads<C::COPIES_DATA>();
   lds_barrier();
 }
 
