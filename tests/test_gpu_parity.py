@@ -70,6 +70,12 @@ CASES = [
          theta=500000.0),
     dict(lengths=[700], ctxs=[0], Hq=32, Hkv=8, D=128, dtype="bf16", block_size=64, p=0.95,
          theta=500000.0, scale=1.0 / np.sqrt(128.0)),
+    # largest query group (G = 32: 8 positions per tile), D = 64, cached keys and a window
+    dict(lengths=[150, 40], ctxs=[33, 200], Hq=64, Hkv=2, D=64, dtype="bf16", block_size=16,
+         p=0.9, theta=500000.0, window=70),
+    # G = 1 at D = 64 with long cached context
+    dict(lengths=[90, 300], ctxs=[1000, 5], Hq=8, Hkv=8, D=64, dtype="bf16", block_size=32,
+         p=0.8, theta=10000.0),
 ]
 
 
