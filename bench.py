@@ -30,8 +30,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+PEAK_F32_VECTOR_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "packed_llama8b"
+OTHER_WORKLOADS = ("small_chunked_fp32", "chunked_128k", "mixed_decode_prefill",
+                   "swa_after_selection")
 
 
 def parse():
@@ -43,12 +46,184 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + OTHER_WORKLOADS,
+                    help="the headline workload (default) or one of the other parity workloads, "
+                         "timed over all of its calls")
     return ap.parse_args()
 
 
 def algorithmic_pairs(call):
     """Visible (query, key) pairs: cached keys plus the causal triangle."""
     return sum(s.n * s.ctx + s.n * (s.n + 1) // 2 for s in call.segments)
+
+
+def visible_pairs(cu, ctx, positions, window):
+    """(query, key) pairs the attention computes for one call: cached keys at
+    positions 0..c-1 plus the segment's own keys, key position <= query
+    position, and within the window when there is one."""
+    total = 0
+    for s in range(len(ctx)):
+        a, b, c = int(cu[s]), int(cu[s + 1]), int(ctx[s])
+        pos = np.asarray(positions[a:b], dtype=np.int64)
+        keys = np.concatenate([np.arange(c, dtype=np.int64), pos])
+        hi = np.searchsorted(keys, pos, side="right")
+        lo = np.searchsorted(keys, pos - window, side="right") if window > 0 else 0
+        total += int(np.sum(hi - lo))
+    return total
+
+
+def run_other_workload(args):
+    """Time every call of a parity workload as one step (inputs resident).
+    The second layer of swa_after_selection runs on the compacted rows at
+    full row capacity (its token count stays on the device)."""
+    import torch
+    import workloads as W
+    from workloads import device as WD
+    from block_sparse_token_amd import binding as B
+    from block_sparse_token_amd import step as ST
+
+    wl = W.make(args.workload)
+    kc, vc = WD.make_caches(wl)
+    calls = []
+    for call in wl.calls:
+        batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
+                              call.block_table)
+        flags = torch.from_numpy(call.flags.astype(np.uint8)).cuda()
+        calls.append((call, ST.PrefillCall(
+            batch=batch, q=WD.stored_to_tensor(call.q), k=WD.stored_to_tensor(call.k),
+            v=WD.stored_to_tensor(call.v), k_cache=kc, v_cache=vc,
+            num_blocks=call.num_blocks(wl.block_size), flags=flags, block_size=wl.block_size,
+            p=wl.p, rope_theta=wl.theta, window=wl.window, rows=WD.row_sources(call))))
+    layer2 = None
+    if wl.layer2:
+        pc = calls[0][1]
+        S = len(calls[0][0].segments)
+        batch2 = B.Batch(pc.cu_seqlens_out, torch.zeros(S, dtype=torch.int32, device="cuda"),
+                         pc.rows_out["positions"], pc.rows_out["slot_mapping"], None)
+        layer2 = ST.PrefillCall(batch=batch2, q=pc.rows_out["q2"], k=pc.rows_out["k2"],
+                                v=pc.rows_out["v2"], k_cache=torch.zeros_like(kc),
+                                v_cache=torch.zeros_like(vc), num_blocks=1, flags=None,
+                                block_size=wl.block_size, p=wl.p,
+                                rope_theta=wl.layer2["theta"], window=wl.layer2["window"])
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def one_step(rec):
+        for _, pc in calls:
+            e = [ev() for _ in range(5)] if rec is not None else None
+            k = (ev(), ev()) if rec is not None else None
+            if rec is not None:
+                B.up_profile_attn_events(*k)
+                e[0].record(stream)
+            pc.attention()
+            if rec is not None:
+                e[1].record(stream)
+            pc.scores_stage()
+            if rec is not None:
+                e[2].record(stream)
+            pc.select_stage()
+            if rec is not None:
+                e[3].record(stream)
+            pc.compact_stage()
+            if rec is not None:
+                e[4].record(stream)
+                rec.append(("call", e, k))
+        if layer2 is not None:
+            k = (ev(), ev()) if rec is not None else None
+            if rec is not None:
+                B.up_profile_attn_events(*k)
+            layer2.attention()
+            if rec is not None:
+                rec.append(("layer2", None, k))
+        if rec is not None:
+            B.up_profile_attn_events()
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    K = args.steps
+    ms_step = wall * 1e3 / K
+    attn = sum(a.elapsed_time(b) for kind, _, (a, b) in recs if kind == "call") / K
+    l2 = sum(a.elapsed_time(b) for kind, _, (a, b) in recs if kind == "layer2") / K
+    st = np.zeros(4)
+    for kind, e, _ in recs:
+        if kind == "call":
+            st += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
+    st /= K
+
+    # algorithmic work
+    e_b = 2 if wl.dtype == "bf16" else 4
+    pairs = sum(visible_pairs(c.cu_seqlens, c.ctx_lens, c.positions, wl.window) for c, _ in calls)
+    flops = 4.0 * wl.D * wl.Hq * pairs
+    T_all = sum(c.T for c, _ in calls)
+    rope_bytes = sum(c.T * (4 * wl.Hkv * wl.D * e_b + 8) for c, _ in calls)
+    kept = [int(pc.num_kept.item()) for _, pc in calls]
+    W_b = wl.hidden_width * e_b
+    # extra row tensors (read and written once per kept row)
+    extra_b = sum(2 * x[0].nbytes for x in calls[0][0].extra.values())
+    compact_bytes = sum(k * (2 * W_b + 20 + extra_b) + c.num_blocks(wl.block_size)
+                        for k, (c, _) in zip(kept, calls))
+    bf16 = wl.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VECTOR_TFLOPS
+    achieved = flops / (attn * 1e-3) / 1e12
+    tokens = T_all
+    res_extra = {}
+    if args.workload == "mixed_decode_prefill":
+        c = calls[0][0]
+        dec = [i for i, s in enumerate(c.segments) if not s.flagged]
+        tokens = int(sum(c.segments[i].n for i in range(len(c.segments)) if c.segments[i].flagged))
+        dec_keys = sum(c.segments[i].ctx + c.segments[i].n for i in dec)
+        dec_bytes = dec_keys * wl.Hkv * wl.D * e_b * 2 + len(dec) * wl.Hq * wl.D * e_b * 2
+        pre_pairs = pairs - sum(c.segments[i].ctx + 1 for i in dec)
+        floor_ms = dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e3 + \
+            4.0 * wl.D * wl.Hq * pre_pairs / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        res_extra["decode_prefill"] = {
+            "decode_segments": len(dec), "decode_kv_bytes": dec_bytes,
+            "prefill_pairs": pre_pairs, "serial_floor_ms": floor_ms,
+            "attention_vs_floor": floor_ms / attn, "all_tokens_per_s": T_all / (ms_step * 1e-3)}
+    if layer2 is not None:
+        nk = kept[0]
+        cu2 = calls[0][1].cu_seqlens_out.cpu().numpy()
+        pos2 = calls[0][1].rows_out["positions"][:nk].cpu().numpy()
+        pairs2 = visible_pairs(cu2, np.zeros(len(cu2) - 1, dtype=np.int64), pos2,
+                               wl.layer2["window"])
+        flops2 = 4.0 * wl.D * wl.Hq * pairs2
+        res_extra["swa_layer"] = {"kept_tokens": nk, "pairs": pairs2, "flops": flops2,
+                                  "ms": l2, "TFLOP/s": flops2 / (l2 * 1e-3) / 1e12,
+                                  "frac": flops2 / (l2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    rope_ms = st[0] - attn
+    res = {
+        "metric": "packed prefill tokens/s (attn+score+select+compact) + % MFMA/HBM roofline",
+        "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "calls": len(calls), "tokens": T_all,
+                   "tokens_counted": tokens, "kept_tokens": kept if len(kept) > 1 else kept[0]},
+        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+                     "avg_ms": attn, "flops_per_step": flops, "pairs": pairs},
+        "stages_ms": {"rope_kv+plan": rope_ms, "attention": attn, "scores": float(st[1]),
+                      "select": float(st[2]), "compact": float(st[3]),
+                      "swa_layer": l2 if layer2 is not None else None},
+        "hbm": {"rope_kv": {"bytes": rope_bytes, "GB/s": rope_bytes / (rope_ms * 1e-3) / 1e9,
+                            "frac": rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                "compact": {"bytes": compact_bytes,
+                            "GB/s": compact_bytes / (st[3] * 1e-3) / 1e9,
+                            "frac": compact_bytes / (st[3] * 1e-3) / 1e9 / PEAK_HBM_GBS}},
+    }
+    res.update(res_extra)
+    print(json.dumps(res), flush=True)
 
 
 def traffic_from_profile(src_hash):
@@ -117,6 +292,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+
+    if args.workload != WORKLOAD:
+        run_other_workload(args)
         return
 
     import workloads as W

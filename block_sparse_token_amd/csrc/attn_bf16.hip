@@ -568,17 +568,20 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   // instructions the other mostly runs the vector softmax.  One extra step
   // lets waves 4-7 finish the last tile.
   const bool lead = w < C::NW / 2;
+  // A wave whose rows all lie past the item's last token (short segments,
+  // decodes) only stages and synchronises.
+  const bool active = __any(rvalid);
   sweep_prologue(st);
   for (int t = 0; t <= nt; ++t) {
     // the two waves of a SIMD issue their copies at different points of the
     // step, so the copies of a step never all queue at once
     if (lead) {
-      if (t < nt) qk(t);
+      if (t < nt && active) qk(t);
       sweep_issue(st, t);
-      if (t < nt) softmax_pv(t);
+      if (t < nt && active) softmax_pv(t);
     } else {
-      if (t > 0) softmax_pv(t - 1);
-      if (t < nt) qk(t);
+      if (t > 0 && active) softmax_pv(t - 1);
+      if (t < nt && active) qk(t);
       sweep_issue(st, t);
     }
     sweep_step_end<C>();

@@ -20,6 +20,7 @@ import torch
 
 import oracle
 import workloads as W
+from workloads import device as WD
 from block_sparse_token_amd import step as ST
 
 F32_REL = 1e-5
@@ -38,24 +39,7 @@ def torch_dtype(wl):
 
 def make_caches(wl, device="cuda"):
     """Zeroed page pools plus any KV that exists before the first call."""
-    shape = (wl.num_pages, wl.Hkv, W.PAGE_SIZE, wl.D)
-    if wl.device_cache_seed is not None:
-        kc = torch.zeros(shape, dtype=torch_dtype(wl), device=device)
-        vc = torch.zeros_like(kc)
-        gen = torch.Generator(device=device)
-        gen.manual_seed(int(wl.device_cache_seed))
-        for pid in sorted(wl.device_cache_ctx):
-            c = wl.device_cache_ctx[pid]
-            pg = torch.from_numpy(wl.prompt_pages[pid].astype(np.int64)).to(device)
-            lp = torch.arange(c, device=device)
-            page, off = pg[lp // W.PAGE_SIZE], lp % W.PAGE_SIZE
-            K = torch.randn((c, wl.Hkv, wl.D), generator=gen, device=device).to(kc.dtype)
-            V = torch.randn((c, wl.Hkv, wl.D), generator=gen, device=device).to(kc.dtype)
-            kc[page, :, off, :] = K
-            vc[page, :, off, :] = V
-        return kc, vc
-    kh, vh = W.paged_given_cache(wl)
-    return ST.stored_to_tensor(kh, device), ST.stored_to_tensor(vh, device)
+    return WD.make_caches(wl, device)
 
 
 def read_back_cache(wl, kc, vc, pid, c):
@@ -67,12 +51,7 @@ def read_back_cache(wl, kc, vc, pid, c):
 
 
 def row_sources(call, device="cuda"):
-    rows = [("hidden", ST.stored_to_tensor(call.hidden, device)),
-            ("positions", torch.from_numpy(call.positions.astype(np.int32)).to(device)),
-            ("slot_mapping", torch.from_numpy(call.slot_mapping.astype(np.int32)).to(device))]
-    for name in sorted(call.extra):
-        rows.append((name, ST.stored_to_tensor(call.extra[name], device)))
-    return rows
+    return WD.row_sources(call, device)
 
 
 def launch_call(wl, call, kc, vc, *, with_lse=True, compact=True, device="cuda", flags=True):
