@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     up_attn_workspace_bytes,
     up_block_offsets,
     up_block_scores,
+    up_check_batch,
     up_compact,
     up_compact_workspace_bytes,
     up_prefill_attn,

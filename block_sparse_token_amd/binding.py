@@ -67,6 +67,7 @@ def lib():
             "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
             "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
             "up_profile_attn_events": (c_i32, [c_vp, c_vp]),
+            "up_check_batch": (c_i32, [bp, c_i32, c_vp, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
         }
@@ -80,7 +81,7 @@ def lib():
 
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
-            "up_compact", "up_profile_attn_events"]
+            "up_compact", "up_profile_attn_events", "up_check_batch"]
 
 
 def _check(st: int, what: str):
@@ -196,3 +197,10 @@ def up_profile_attn_events(start=None, stop=None):
     hs = ctypes.c_void_p(start.cuda_event) if start is not None else None
     he = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
     _check(lib().up_profile_attn_events(hs, he), "up_profile_attn_events")
+
+
+def up_check_batch(batch: Batch, num_pages: int, err_word, stream=None):
+    """Check the batch's device-side preconditions (synchronises the stream);
+    raises UniprefillError naming every violated condition."""
+    _check(lib().up_check_batch(batch.ref, int(num_pages), _p(err_word), _stream(stream)),
+           "up_check_batch")

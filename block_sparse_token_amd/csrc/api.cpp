@@ -1,9 +1,10 @@
 // Host side of the C ABI declared in include/uniprefill.h: argument
-// validation, workspace carving and kernel launches.  No allocation, no
-// synchronisation, no device state.
+// validation, workspace carving and kernel launches.  No allocation and no
+// device state; only the batch check (a debug aid) synchronises.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include "../../include/uniprefill.h"
 #include "common.h"
@@ -51,6 +52,42 @@ up_status check_batch(const up_batch* b, bool need_positions) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// UP_DEBUG_CHECKS=1 in the environment: up_prefill_attn checks the batch's
+// device-side preconditions first (and synchronises on the result).
+bool debug_checks() {
+  const char* v = getenv("UP_DEBUG_CHECKS");
+  return v && atoi(v) != 0;
+}
+
+up_status run_check(const up_batch* b, int32_t num_pages, int32_t* err, hipStream_t st) {
+  hipError_t e = up::launch_check_batch(b->cu_seqlens, b->ctx_lens, b->positions,
+                                        b->slot_mapping, b->block_table, b->num_seqs,
+                                        b->num_tokens, b->max_pages, num_pages, err, st);
+  if (e != hipSuccess) return device_status(e, "batch check launch");
+  int32_t bits = 0;
+  e = hipMemcpyAsync(&bits, err, sizeof bits, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return device_status(e, "batch check read-back");
+  if (!bits) return UP_OK;
+  static const char* what[] = {"cu_seqlens[0] != 0",
+                               "a segment has no token",
+                               "cu_seqlens[S] > num_tokens",
+                               "negative ctx_lens",
+                               "positions not increasing inside a segment or below ctx_len",
+                               "slot out of range",
+                               "page id out of range",
+                               "block table too short or missing for cached tokens"};
+  std::string msg = "batch check failed:";
+  for (int i = 0; i < 8; ++i)
+    if (bits & (1 << i)) {
+      msg += " ";
+      msg += what[i];
+      msg += ";";
+    }
+  g_err = msg;
+  return UP_ERR_INVALID;
+}
+
 int positions_per_tile(up_dtype dt, int D, int G) {
   return dt == UP_BF16 ? up::attn_bf16_positions_per_tile(D, G)
                        : up::attn_f32_positions_per_tile(D, G);
@@ -63,6 +100,15 @@ extern "C" {
 const char* up_last_error(void) { return g_err.c_str(); }
 
 const char* up_version(void) { return "uniprefill 0.1 gfx950"; }
+
+up_status up_check_batch(const up_batch* batch, int32_t num_pages, int32_t* err_word,
+                         void* stream) {
+  up_status st = check_batch(batch, true);
+  if (st) return st;
+  if (!err_word) return fail(UP_ERR_INVALID, "err_word is NULL");
+  if (num_pages < 0) return fail(UP_ERR_INVALID, "num_pages must be >= 0 (got %d)", num_pages);
+  return run_check(batch, num_pages, err_word, as_stream(stream));
+}
 
 up_status up_profile_attn_events(void* attn_start, void* attn_stop) {
   if ((attn_start == nullptr) != (attn_stop == nullptr))
@@ -130,6 +176,10 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
     return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
 
   hipStream_t s = as_stream(stream);
+  if (debug_checks()) {
+    st = run_check(batch, 0, (int32_t*)workspace, s);
+    if (st) return st;
+  }
   const bool bf16 = dtype == UP_BF16;
   const int P = positions_per_tile(dtype, D, G);
   const int cap = (int)up::work_capacity(batch->num_tokens, batch->num_seqs, P);

@@ -63,6 +63,19 @@ struct RopeArgs {
 
 // ---------------------------------------------------------------- launchers
 // All return hipSuccess or the launch error.
+// violation bits reported by launch_check_batch
+constexpr int kCheckCuStart = 1 << 0;     // cu_seqlens[0] != 0
+constexpr int kCheckSegment = 1 << 1;     // a segment with fewer than one token
+constexpr int kCheckCuEnd = 1 << 2;       // cu_seqlens[S] > num_tokens
+constexpr int kCheckCtx = 1 << 3;         // ctx_lens < 0
+constexpr int kCheckPositions = 1 << 4;   // not strictly increasing, or first < ctx
+constexpr int kCheckSlots = 1 << 5;       // slot < -1 or beyond the page pool
+constexpr int kCheckPages = 1 << 6;       // page id < 0 or beyond the page pool
+constexpr int kCheckBlockTable = 1 << 7;  // table too short for ctx + n, or missing
+hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                              const int32_t* positions, const int32_t* slot_mapping,
+                              const int32_t* block_table, int S, int T, int max_pages,
+                              int num_pages, int32_t* err, hipStream_t st);
 hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,
                                 int32_t* cu_blocks, hipStream_t st);
 hipError_t launch_plan(const int32_t* cu_seqlens, const int32_t* ctx_lens,

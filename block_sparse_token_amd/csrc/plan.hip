@@ -133,6 +133,61 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Device-side preconditions of a batch, as violation bits OR-ed into
+// err[0] (see kCheck* in common.h).  One thread per segment walks its
+// tokens; every index is clamped into its array, so a malformed batch is
+// reported, never followed.
+__global__ __launch_bounds__(256) void check_zero_kernel(int32_t* err) {
+  if (threadIdx.x == 0) err[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void check_batch_kernel(const int32_t* __restrict__ cu_seqlens,
+                                                          const int32_t* __restrict__ ctx_lens,
+                                                          const int32_t* __restrict__ positions,
+                                                          const int32_t* __restrict__ slot_mapping,
+                                                          const int32_t* __restrict__ block_table,
+                                                          int S, int T, int max_pages,
+                                                          int num_pages, int32_t* err) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
+  int bits = 0;
+  if (s == 0 && cu_seqlens[0] != 0) bits |= kCheckCuStart;
+  if (s == S - 1 && cu_seqlens[S] > T) bits |= kCheckCuEnd;
+  const int a = min(max(cu_seqlens[s], 0), T), b = min(max(cu_seqlens[s + 1], 0), T);
+  if (cu_seqlens[s + 1] - cu_seqlens[s] < 1) bits |= kCheckSegment;
+  const int c = ctx_lens[s];
+  if (c < 0) bits |= kCheckCtx;
+  for (int t = a; t < b; ++t) {
+    const int p = positions[t];
+    if (t == a ? p < c : p <= positions[t - 1]) bits |= kCheckPositions;
+    const int sl = slot_mapping[t];
+    if (sl < 0 || (num_pages > 0 && sl >= num_pages * kPageSize)) bits |= kCheckSlots;
+  }
+  if (block_table) {
+    const long need = ((long)max(c, 0) + kPageSize - 1) / kPageSize;
+    if (need > max_pages) bits |= kCheckBlockTable;
+    const int m = (int)min(need, (long)max_pages);
+    for (int i = 0; i < m; ++i) {
+      const int pg = block_table[(long)s * max_pages + i];
+      if (pg < 0 || (num_pages > 0 && pg >= num_pages)) bits |= kCheckPages;
+    }
+  } else if (c > 0) {
+    bits |= kCheckBlockTable;
+  }
+  if (bits) atomicOr(err, bits);
+}
+
+hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                              const int32_t* positions, const int32_t* slot_mapping,
+                              const int32_t* block_table, int S, int T, int max_pages,
+                              int num_pages, int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(check_zero_kernel, dim3(1), dim3(64), 0, st, err);
+  hipLaunchKernelGGL(check_batch_kernel, dim3((S + 255) / 256), dim3(256), 0, st, cu_seqlens,
+                     ctx_lens, positions, slot_mapping, block_table, S, T, max_pages, num_pages,
+                     err);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan(const int32_t* cu_seqlens, const int32_t* ctx_lens,
                        const uint8_t* score_flags, int S, int positions_per_tile, int window,
                        int2* items, int32_t* count, int capacity, hipStream_t st) {

@@ -32,7 +32,8 @@
  *    capacities named below), KV caches and workspaces.  The library
  *    allocates and frees no memory and keeps no device state.
  *  - Every call is asynchronous on ``stream`` (a hipStream_t; NULL = the
- *    null stream) and never synchronises.
+ *    null stream) and never synchronises, except the debug aid
+ *    up_check_batch (and up_prefill_attn with UP_DEBUG_CHECKS set).
  *  - Arguments are validated on the host before any launch; on failure the
  *    call returns a negative status, launches nothing, writes no output and
  *    sets the text returned by up_last_error() for the calling thread.  A
@@ -219,6 +220,24 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
  * turns it off.  The events must outlive the calls that record them.
  */
 up_status up_profile_attn_events(void* attn_start, void* attn_stop);
+
+/*
+ * Debug aid (not part of the operator): checks the batch's device-side
+ * preconditions listed at the top of this header on the device, reading
+ * only inside each array's extent (cu_seqlens [S+1], ctx_lens [S],
+ * positions and slot_mapping [T], block_table [S, max_pages]).  num_pages
+ * > 0 also checks page ids and slots against a cache of num_pages pages;
+ * 0 skips those two range checks.  err_word: one int32 of device scratch.
+ * Synchronises ``stream``; returns UP_OK, or UP_ERR_INVALID with
+ * up_last_error() naming every violated condition.
+ *
+ * With the environment variable UP_DEBUG_CHECKS set to a non-zero integer
+ * (read on every call), up_prefill_attn runs this check (num_pages = 0,
+ * the workspace's first word as err_word) before it launches anything, and
+ * returns its status if the batch fails it.
+ */
+up_status up_check_batch(const up_batch* batch, int32_t num_pages, int32_t* err_word,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -123,3 +123,15 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(4, dtype=torch.int32)
     with pytest.raises(Bd.UniprefillError):
         Bd.Batch(t, t, t, t)
+
+
+def test_batch_check_argument_validation(L):
+    b = _batch()
+    assert L.up_check_batch(None, 0, FAKE, None) == UP_ERR_INVALID
+    assert L.up_check_batch(ctypes.byref(b), 0, None, None) == UP_ERR_INVALID
+    assert "err_word" in L.up_last_error().decode()
+    assert L.up_check_batch(ctypes.byref(b), -1, FAKE, None) == UP_ERR_INVALID
+    assert L.up_check_batch(ctypes.byref(_batch(page_size=8)), 0, FAKE, None) == UP_ERR_UNSUPPORTED
+    nopos = _batch()
+    nopos.positions = None
+    assert L.up_check_batch(ctypes.byref(nopos), 0, FAKE, None) == UP_ERR_INVALID
