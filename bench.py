@@ -11,8 +11,11 @@ are synthetic and resident on the GPU before timing starts.
 Prints one JSON line.  ``roofline`` covers the attention kernel (the
 dominant one): algorithmic flops 4 * D * Hq * (causal in-segment query/key
 pairs) per launch over its average duration, timed with HIP events recorded
-by the library around that kernel on its stream.  ``cpu_baseline`` is the
-float64 NumPy oracle timed on this host on a sample of the same batch.
+by the library around that kernel on its stream; ``attainable`` beside the
+published ``peak`` is what a plain bf16 matrix-core loop sustains on the
+same GPU in the same run (and ``attainable_peaks`` the copy rate too).
+``cpu_baseline`` is the float64 NumPy oracle timed on this host on a sample
+of the same batch.
 """
 from __future__ import annotations
 
@@ -240,6 +243,42 @@ def traffic_from_profile(src_hash):
     return float(t.group(1))
 
 
+def attainable_peaks(torch, B, stream):
+    """What the chip sustains: a bf16 matrix-core loop (2048 workgroups of
+    four waves, about 10 ms a launch) and a 1 GiB device-to-device copy,
+    each the median of several event-timed launches after a warm-up."""
+    wgs, iters = 2048, 16384
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    flops = wgs * 4.0 * iters * 4 * 32768
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    mfma_ms = timed(lambda: B.up_peak_mfma_bf16(wgs, iters, sink), 5)
+    copy_ms = timed(lambda: B.up_peak_copy(src, dst), 10)
+    if not torch.equal(dst[:: 1 << 20], src[:: 1 << 20]):
+        raise RuntimeError("peak copy produced wrong data")
+    del src, dst, sink
+    return {"mfma_bf16_TFLOP/s": flops / (mfma_ms * 1e-3) / 1e12,
+            "hbm_copy_GB/s": 2.0 * n / (copy_ms * 1e-3) / 1e9,
+            "method": "up_peak_mfma_bf16 (2048 x 4 waves, 4 independent 32x32x16 chains) and "
+                      "up_peak_copy (1 GiB read + 1 GiB written), medians of event-timed launches"}
+
+
 def cpu_baseline(wl, call, budget_s):
     """Time the oracle on whole prompts of the batch, picked near the
     token-weighted mean length (attention cost per token grows with length),
@@ -393,6 +432,11 @@ def main():
                         "GB/s": compact_bytes / (st_mean[3] * 1e-3) / 1e9,
                         "frac": compact_bytes / (st_mean[3] * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
+    att = attainable_peaks(torch, B, stream)
+    res["roofline"]["attainable"] = att["mfma_bf16_TFLOP/s"]
+    res["roofline"]["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOP/s"]
+    res["attainable_peaks"] = att
+    res["compact_hbm"]["frac_of_attainable"] = res["compact_hbm"]["GB/s"] / att["hbm_copy_GB/s"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
     print(json.dumps(res), flush=True)

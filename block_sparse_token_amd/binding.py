@@ -68,6 +68,8 @@ def lib():
             "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
             "up_profile_attn_events": (c_i32, [c_vp, c_vp]),
             "up_check_batch": (c_i32, [bp, c_i32, c_vp, c_vp]),
+            "up_peak_mfma_bf16": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
+            "up_peak_copy": (c_i32, [c_vp, c_vp, c_size, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
         }
@@ -81,7 +83,8 @@ def lib():
 
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
-            "up_compact", "up_profile_attn_events", "up_check_batch"]
+            "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
+            "up_peak_copy"]
 
 
 def _check(st: int, what: str):
@@ -204,3 +207,19 @@ def up_check_batch(batch: Batch, num_pages: int, err_word, stream=None):
     raises UniprefillError naming every violated condition."""
     _check(lib().up_check_batch(batch.ref, int(num_pages), _p(err_word), _stream(stream)),
            "up_check_batch")
+
+
+def up_peak_mfma_bf16(workgroups: int, iters: int, sink, stream=None):
+    """bf16 matrix-core loop: workgroups * 4 * iters * 4 * 32768 flops."""
+    if sink.numel() * sink.element_size() < workgroups * 256 * 4:
+        raise UniprefillError("sink must hold workgroups * 256 floats")
+    _check(lib().up_peak_mfma_bf16(int(workgroups), int(iters), _p(sink), _stream(stream)),
+           "up_peak_mfma_bf16")
+
+
+def up_peak_copy(src, dst, stream=None):
+    """Copy src to dst (same byte size) with the library's streaming copy."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise UniprefillError("dst is smaller than src")
+    _check(lib().up_peak_copy(_p(src), _p(dst), n, _stream(stream)), "up_peak_copy")

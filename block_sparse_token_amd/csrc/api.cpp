@@ -118,6 +118,21 @@ up_status up_profile_attn_events(void* attn_start, void* attn_stop) {
   return UP_OK;
 }
 
+up_status up_peak_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  if (workgroups < 1 || iters < 1)
+    return fail(UP_ERR_INVALID, "workgroups and iters must be >= 1 (got %d, %d)", workgroups, iters);
+  if (!sink) return fail(UP_ERR_INVALID, "sink is NULL");
+  return device_status(up::launch_peak_mfma(workgroups, iters, sink, as_stream(stream)),
+                       "peak mfma launch");
+}
+
+up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(UP_ERR_INVALID, "src and dst must be non-NULL");
+  if ((((uintptr_t)src) | ((uintptr_t)dst) | bytes) & 15)
+    return fail(UP_ERR_INVALID, "src, dst and bytes must be multiples of 16");
+  return device_status(up::launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak copy launch");
+}
+
 up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
                            void* stream) {
   up_status st = check_batch(batch, false);

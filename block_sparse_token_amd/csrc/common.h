@@ -76,6 +76,8 @@ hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens
                               const int32_t* positions, const int32_t* slot_mapping,
                               const int32_t* block_table, int S, int T, int max_pages,
                               int num_pages, int32_t* err, hipStream_t st);
+hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
+hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,
                                 int32_t* cu_blocks, hipStream_t st);
 hipError_t launch_plan(const int32_t* cu_seqlens, const int32_t* ctx_lens,

@@ -222,6 +222,20 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
 up_status up_profile_attn_events(void* attn_start, void* attn_stop);
 
 /*
+ * Measurement aids (not part of the operator): what the chip sustains, to
+ * set beside its published peaks.
+ *  - up_peak_mfma_bf16: `workgroups` workgroups of four waves; every wave
+ *    runs iters x 4 bf16 products of 32x32x16 (32768 flops each), so one
+ *    launch does workgroups * 4 * iters * 4 * 32768 flops.  sink: [workgroups
+ *    * 256] float output (a fold of the accumulators, no meaning).
+ *  - up_peak_copy: copies `bytes` (a multiple of 16; src and dst 16-byte
+ *    aligned, not overlapping) from src to dst with 16-byte loads and stores.
+ * Both are asynchronous on ``stream``; time them with events.
+ */
+up_status up_peak_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream);
+up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/*
  * Debug aid (not part of the operator): checks the batch's device-side
  * preconditions listed at the top of this header on the device, reading
  * only inside each array's extent (cu_seqlens [S+1], ctx_lens [S],

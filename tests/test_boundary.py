@@ -135,3 +135,12 @@ def test_batch_check_argument_validation(L):
     nopos = _batch()
     nopos.positions = None
     assert L.up_check_batch(ctypes.byref(nopos), 0, FAKE, None) == UP_ERR_INVALID
+
+
+def test_peak_probe_argument_validation(L):
+    assert L.up_peak_mfma_bf16(0, 10, FAKE, None) == UP_ERR_INVALID
+    assert L.up_peak_mfma_bf16(4, 0, FAKE, None) == UP_ERR_INVALID
+    assert L.up_peak_mfma_bf16(4, 10, None, None) == UP_ERR_INVALID
+    assert L.up_peak_copy(FAKE, None, 16, None) == UP_ERR_INVALID
+    assert L.up_peak_copy(FAKE, FAKE, 24, None) == UP_ERR_INVALID
+    assert L.up_peak_copy(ctypes.c_void_p(0x1008), FAKE, 16, None) == UP_ERR_INVALID
