@@ -170,7 +170,7 @@ def _pages_for(rng, prompt_len: dict):
 
 
 def _pack_calls(schedule, prompt_pages, Hq, Hkv, D, W, dtype, rng, scale, heavy_tok, u,
-                draw_hidden=True):
+                draw_hidden=True, q_mult=1.0):
     """Draw q, k, v, hidden for every new token of the schedule and pack per call.
 
     ``schedule``: list of calls, each a list of Segment.  ``heavy_tok``: dict
@@ -178,6 +178,8 @@ def _pack_calls(schedule, prompt_pages, Hq, Hkv, D, W, dtype, rng, scale, heavy_
     """
     tot = sum(s.n for call in schedule for s in call)
     q = _normal32(rng, (tot, Hq, D), scale)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
     k = _normal32(rng, (tot, Hkv, D), scale)
     v = _normal32(rng, (tot, Hkv, D), scale)
     # heavy-hitter keys
@@ -395,10 +397,11 @@ def make(name: str, seed: int | None = None, **kw) -> Workload:
 # ---------------------------------------------------------------------------
 def custom(*, lengths, ctxs=None, flags=None, Hq=2, Hkv=2, D=64, dtype="f32", block_size=16,
            p=0.9, theta=0.0, window=0, hidden_width=64, seed=0, heavy_frac=0.1, scale=1.0,
-           extra_rows=False, layer2_window=0) -> Workload:
+           extra_rows=False, layer2_window=0, q_mult=1.0) -> Workload:
     """One call with the given segments.  A segment with ctx > 0 has ``ctx``
     cached tokens drawn here (taken as already rotated) and written into its
-    pages before the call."""
+    pages before the call.  ``q_mult`` multiplies the query draws only (large
+    logits without larger values)."""
     rng = np.random.default_rng(seed)
     S = len(lengths)
     ctxs = list(ctxs) if ctxs is not None else [0] * S
@@ -413,7 +416,8 @@ def custom(*, lengths, ctxs=None, flags=None, Hq=2, Hkv=2, D=64, dtype="f32", bl
         heavy[i] = h
     u = _unit(rng, D)
     segs = [Segment(prompt=i, ctx=ctxs[i], n=lengths[i], flagged=bool(flags[i])) for i in range(S)]
-    qs, ks, vs, hs = _pack_calls([segs], None, Hq, Hkv, D, hidden_width, dtype, rng, scale, heavy, u)
+    qs, ks, vs, hs = _pack_calls([segs], None, Hq, Hkv, D, hidden_width, dtype, rng, scale, heavy, u,
+                                 q_mult=q_mult)
     npages, pages = _pages_for(rng, plen)
     calls = _finish_calls([segs], qs, ks, vs, hs, pages)
     wl = Workload(name="custom", dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size, p=p,
