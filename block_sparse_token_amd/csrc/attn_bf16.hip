@@ -25,13 +25,18 @@
 //    of three tile buffers.  Each wave waits only for its own copies of the
 //    next tile (an exact count of its outstanding copies), then one barrier
 //    per tile publishes it.
-//  * Online softmax in exp2 with the scale folded in and a lazily raised
-//    running max (rescale only when a tile's max is 2^8 above it).
+//  * Softmax in exp2 with the scale folded in, against a per-row reference
+//    max fixed at the row's first tile with a visible key: the steady loop
+//    computes no row max and never rescales O.  A tile whose probabilities
+//    pass 2^64 sends the item through a second loop with a running max that
+//    is raised (and O, l rescaled) when a tile's max is 2^8 above it.
 //  * Score items: for a scored segment and KV head, a first QK^T sweep over
 //    every visible key gives the exact softmax normaliser of the rows of the
 //    segment's last query block; a second sweep over the segment's own keys
 //    sums those probabilities per key block.  The result is written to
 //    block_mass[block, head] in a fixed order (deterministic).
+#include <type_traits>
+
 #include "common.h"
 
 namespace up {
@@ -459,6 +464,8 @@ __device__ inline float scaled_row_max(const f32x16 (&s)[2], float sl2) {
 // against the stale max and stay below 2^kLazy, exact after the final
 // division by l.
 constexpr float kLazy = 8.0f;
+constexpr float kRefUnset = -1.0e29f;         // ms above this: a reference is set
+constexpr float kRefMaxSum = 1.8446744e19f;   // 2^64
 
 template <class C>
 __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
@@ -489,12 +496,8 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const float sl2 = a.scale_log2;
 
   f32x16 o[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-  float ms = kNegBig, lsum = 0.f;  // running max (log2 units) and partial row sum
-  f32x16 sacc[2];                  // S^T of the tile between QK and softmax
+  float ms, lsum;   // reference or running max (log2 units), partial row sum
+  f32x16 sacc[2];   // S^T of the tile between QK and softmax
 
   const int t0 = (u_lo / C::BN) * C::BN;
   const int nt = (u_end - t0 + C::BN - 1) / C::BN;
@@ -513,20 +516,9 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
     if (!full) apply_mask(kpos, qpos, window, sacc);
   };
-  // softmax of S^T (tile t) and O^T += V^T P^T
-  auto softmax_pv = [&](int t) {
+  // probabilities of S^T (tile t) against ms, their row sum, O^T += V^T P^T
+  auto probs_pv = [&](int t) {
     const TileFrag<C> tf(fo, l0 + st.buf_off(t));
-    const float mx = scaled_row_max(sacc, sl2);
-    if (__any(mx > ms + kLazy)) {
-      const float mnew = fmaxf(ms, mx);
-      const float alpha = __builtin_amdgcn_exp2f(ms - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-      ms = mnew;
-    }
     bf16x8 pf[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -543,7 +535,8 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][4], pf[ks][5]}, one2, rs0, false);
       rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, rs1, false);
     }
-    lsum += rs0 + rs1;
+    const float rs = rs0 + rs1;
+    lsum += rs;
     // 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2.  V^T
     // fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 + 0..3 and
     // ks*16 + 8 + h*4 + 0..3 at d, via two transpose reads in which lane
@@ -560,6 +553,39 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
     }
+    return rs;
+  };
+  // Fast path (reference max): a row's reference is its max over its first
+  // tile with a visible key (before that O and l are zero, so setting it
+  // costs nothing) and stays fixed, so the steady loop has no row max and
+  // no rescaling.  Later probabilities may exceed 1: bf16 and fp32 keep
+  // their relative precision there and the final division by l
+  // normalises.  A tile whose row sum passes 2^64 marks the item, which is
+  // then recomputed by the rescaling path.
+  bool bad = false;
+  auto softmax_pv_ref = [&](int t) {
+    if (__any(ms <= kRefUnset)) {
+      const float mx = scaled_row_max(sacc, sl2);
+      ms = ms > kRefUnset ? ms : fmaxf(ms, mx);
+    }
+    const float rs = probs_pv(t);
+    bad = bad || !(rs <= kRefMaxSum);
+  };
+  // Rescaling path: the running max is raised (and O, l rescaled) when a
+  // tile's max exceeds it by more than kLazy.
+  auto softmax_pv_rescale = [&](int t) {
+    const float mx = scaled_row_max(sacc, sl2);
+    if (__any(mx > ms + kLazy)) {
+      const float mnew = fmaxf(ms, mx);
+      const float alpha = __builtin_amdgcn_exp2f(ms - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      ms = mnew;
+    }
+    probs_pv(t);
   };
 
   // The two waves that share a SIMD (w and w+4) work on different stages:
@@ -571,22 +597,41 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   // A wave whose rows all lie past the item's last token (short segments,
   // decodes) only stages and synchronises.
   const bool active = __any(rvalid);
-  sweep_prologue(st);
-  for (int t = 0; t <= nt; ++t) {
-    // the two waves of a SIMD issue their copies at different points of the
-    // step, so the copies of a step never all queue at once
-    if (lead) {
-      if (t < nt && active) qk(t);
-      sweep_issue(st, t);
-      if (t < nt && active) softmax_pv(t);
-    } else {
-      if (t > 0 && active) softmax_pv(t - 1);
-      if (t < nt && active) qk(t);
-      sweep_issue(st, t);
+  auto run = [&](auto rescale) {
+    constexpr bool R = decltype(rescale)::value;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+    ms = kNegBig;
+    lsum = 0.f;
+    auto spv = [&](int t) {
+      if constexpr (R) softmax_pv_rescale(t);
+      else softmax_pv_ref(t);
+    };
+    sweep_prologue(st);
+    for (int t = 0; t <= nt; ++t) {
+      // the two waves of a SIMD issue their copies at different points of
+      // the step, so the copies of a step never all queue at once
+      if (lead) {
+        if (t < nt && active) qk(t);
+        sweep_issue(st, t);
+        if (t < nt && active) spv(t);
+      } else {
+        if (t > 0 && active) spv(t - 1);
+        if (t < nt && active) qk(t);
+        sweep_issue(st, t);
+      }
+      sweep_step_end<C>();
     }
-    sweep_step_end<C>();
-  }
-  wait_loads<0>();
+    wait_loads<0>();
+  };
+  int* misc = (int*)(lds + C::MISC_OFF);
+  if (tid == 0) misc[1] = 0;  // published by the prologue's barriers
+  run(std::false_type{});
+  if (__any(bad) && l == 0) misc[1] = 1;
+  lds_barrier();
+  if (misc[1]) run(std::true_type{});
 
   // epilogue: normalise and store; lane holds d = db*32 + jg*8 + h*4 + e
   const float ltot = pair_sum(lsum);
