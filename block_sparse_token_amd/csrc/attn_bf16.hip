@@ -222,25 +222,34 @@ struct Stager {
     const int* rv = (const int*)(lds + ring_off(k));
     int* rp = (int*)(lds + ring_off(k) + C::BN * 4);
     const uint32_t dst = l0 + buf_off(k);
+    const int pc = lane % C::CPR;
+    // every ring entry this wave needs, in one round trip
+    int val[C::WPW];
+#pragma unroll
+    for (int x = 0; x < C::WPW; ++x) val[x] = rv[w * C::KPW + x * C::RPW + lane / C::CPR];
 #pragma unroll
     for (int x = 0; x < C::WPW; ++x) {
       const int rbase = w * C::KPW + x * C::RPW;
       const int r = rbase + lane / C::CPR;
-      const int u = u0 + r;
-      const int uu = min(u, u_end - 1);
+      const int uu = min(u0 + r, u_end - 1);
       const bool cached = uu < sg.c;
-      const int val = rv[r];
-      const int page = cached ? val : (val >> 4);
-      const int off = cached ? (uu & 15) : (val & 15);
+      const int page = cached ? val[x] : (val[x] >> 4);
+      const int off = cached ? (uu & 15) : (val[x] & 15);
       // 24-bit product: Hkv <= 255 (checked by the host), page * Hkv < 2^27
       // (a documented precondition on the cache size)
       const long rowb = (long)((__umul24(page, a.Hkv) + g) * kPageSize + off) * C::RBYTES;
-      const int pc = lane % C::CPR;
       copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,
              dst + C::K_OFF + rbase * C::RBYTES);
       copy16((uintptr_t)a.v_cache + rowb + (pc ^ swv<C::D>(r)) * 16,
              dst + C::V_OFF + rbase * C::RBYTES);
-      if (pc == 0) rp[r] = u < u_end ? (cached ? uu : rp[r]) : kPosInvalid;
+    }
+    // positions: a cached key's is its index, one past the visible range
+    // gets INT_MAX; an own key keeps the copied one (no write)
+#pragma unroll
+    for (int x = 0; x < C::WPW; ++x) {
+      const int r = w * C::KPW + x * C::RPW + lane / C::CPR;
+      const int u = u0 + r;
+      if (pc == 0 && (u >= u_end || u < sg.c)) rp[r] = u < u_end ? u : kPosInvalid;
     }
   }
 };
