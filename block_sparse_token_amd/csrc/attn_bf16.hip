@@ -22,9 +22,10 @@
 //  * Key tiles of 64 arrive by direct global->LDS copies (no staging
 //    registers): the cache-row index and position of every key four tiles
 //    ahead go to a small LDS ring, the K and V rows two tiles ahead go to one
-//    of three tile buffers.  Each wave waits only for its own copies of the
-//    next tile (an exact count of its outstanding copies), then one barrier
-//    per tile publishes it.
+//    of four tile buffers (a tile is read in two steps: waves 4-7 finish it
+//    one step late).  Each wave waits only for its own copies of the next
+//    tile (an exact count of its outstanding copies), then one barrier per
+//    tile publishes it.
 //  * Softmax in exp2 with the scale folded in, against a per-row reference
 //    max fixed at the row's first tile with a visible key: the steady loop
 //    computes no row max and never rescales O.  A tile whose probabilities
