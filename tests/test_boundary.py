@@ -73,6 +73,8 @@ def test_attention_argument_validation(L):
     assert _attn(L, _batch(page_size=8)) == UP_ERR_UNSUPPORTED
     assert _attn(L, _batch(S=0)) == UP_ERR_INVALID
     assert _attn(L, _batch(S=5, T=3)) == UP_ERR_INVALID
+    assert _attn(L, _batch(S=4097, T=5000)) == UP_ERR_UNSUPPORTED  # work planner limit
+    assert "4096" in L.up_last_error().decode()
     assert _attn(L, b, flags=FAKE, block=48) == UP_ERR_UNSUPPORTED
     assert _attn(L, b, theta=float("nan")) == UP_ERR_INVALID
     need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128)

@@ -92,3 +92,16 @@ def test_gpu_fuzz_cases(idx):
     kw = dict(CASES[idx])
     wl = W.custom(seed=1000 + idx, hidden_width=64, **kw)
     assert _run_and_check(wl)
+
+
+def test_gpu_most_segments_per_call():
+    """4096 segments (the planner's limit) of 1..9 tokens, some with cached
+    prefixes, alternate segments scored."""
+    rng = np.random.default_rng(5)
+    S = 4096
+    lengths = [int(x) for x in rng.integers(1, 10, size=S)]
+    ctxs = [int(x) if i % 3 == 0 else 0 for i, x in enumerate(rng.integers(1, 40, size=S))]
+    flags = [i % 2 == 0 for i in range(S)]
+    wl = W.custom(seed=4096, hidden_width=16, lengths=lengths, ctxs=ctxs, flags=flags, Hq=4,
+                  Hkv=2, D=64, dtype="bf16", block_size=16, p=0.9, theta=500000.0)
+    assert _run_and_check(wl)
