@@ -230,7 +230,7 @@ __device__ void score_item_f(const AttnArgs& a, int s, int g, char* lds) {
       red[threadIdx.x * 2 + 0] = part[0];
       red[threadIdx.x * 2 + 1] = part[1];
       __syncthreads();
-      if (threadIdx.x < nbt * G) {
+      if ((int)threadIdx.x < nbt * G) {
         const int bt = threadIdx.x / G, h2 = threadIdx.x % G;
         float tot = 0.f;
         for (int t = h2; t < NT; t += G) tot += red[t * 2 + bt];  // fixed order

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __rest
                                                          uint32_t p_fx, int keep_all) {
   __shared__ unsigned long long hq[256];
   __shared__ unsigned long long red[kSelThreads];
-  __shared__ unsigned long long s_need, s_above, s_carry;
+  __shared__ unsigned long long s_need, s_carry;
   __shared__ uint32_t s_prefix;
   __shared__ int s_kept;
   const int tid = threadIdx.x;
@@ -110,7 +110,6 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __rest
     const unsigned long long target = ((unsigned long long)p_fx * Q + ((1ull << 22) - 1)) >> 22;
     const unsigned long long forced = fx_score(sc[0]) + fx_score(sc[nb - 1]);
     s_need = target > forced ? target - forced : 0ull;
-    s_above = 0;
     s_prefix = 0;
     s_kept = 2;
     s_carry = 0;
@@ -180,7 +179,6 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __rest
       if (lane == first) {
         const int bstar = hit >= 0 ? 255 - 4 * lane - hit : 0;
         s_need = need - cum;
-        s_above += cum;
         s_prefix = prefix | ((uint32_t)bstar << shift);
       }
     }
