@@ -277,6 +277,27 @@ __device__ inline void sweep_issue(const Stager<C>& st, int t) {
   st.index(t + C::IA);
   st.data(t + C::LA);
 }
+// Attention items copy only tiles that exist: step t issues the index
+// copies of tile t+IA and the data copies of tile t+LA only while those are
+// below nt, and waits for everything but what it issued.
+template <class C>
+__device__ inline void sweep_issue_bounded(const Stager<C>& st, int t, int nt) {
+  if (t + C::IA < nt) st.index(t + C::IA);
+  if (t + C::LA < nt) st.data(t + C::LA);
+}
+template <class C>
+__device__ inline void sweep_step_end_bounded(int t, int nt) {
+  const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  if (t + C::IA < nt) {
+    if (w0) wait_loads<C::COPIES_STEP>();
+    else wait_loads<C::COPIES_DATA>();
+  } else if (t + C::LA < nt) {
+    wait_loads<C::COPIES_DATA>();
+  } else {
+    wait_loads<0>();
+  }
+  lds_barrier();
+}
 template <class C>
 __device__ inline void sweep_step_end() {
   // everything but this step's copies (wave 0 also issued the index copies):
@@ -601,8 +622,8 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   // The two waves that share a SIMD (w and w+4) work on different stages:
   // waves 0-3 run QK, softmax and PV of tile t in step t; waves 4-7 run
   // softmax and PV of tile t-1, then QK of tile t.  While one issues matrix
-  // instructions the other mostly runs the vector softmax.  One extra step
-  // lets waves 4-7 finish the last tile.
+  // instructions the other mostly runs the vector softmax.  Waves 4-7 finish
+  // the last tile after the loop.
   const bool lead = w < C::NW / 2;
   // A wave whose rows all lie past the item's last token (short segments,
   // decodes) only stages and synchronises.
@@ -620,20 +641,22 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       else softmax_pv_ref(t);
     };
     sweep_prologue(st);
-    for (int t = 0; t <= nt; ++t) {
+    for (int t = 0; t < nt; ++t) {
       // the two waves of a SIMD issue their copies at different points of
       // the step, so the copies of a step never all queue at once
       if (lead) {
-        if (t < nt && active) qk(t);
-        sweep_issue(st, t);
-        if (t < nt && active) spv(t);
+        if (active) qk(t);
+        sweep_issue_bounded(st, t, nt);
+        if (active) spv(t);
       } else {
         if (t > 0 && active) spv(t - 1);
-        if (t < nt && active) qk(t);
-        sweep_issue(st, t);
+        if (active) qk(t);
+        sweep_issue_bounded(st, t, nt);
       }
-      sweep_step_end<C>();
+      sweep_step_end_bounded<C>(t, nt);
     }
+    // waves 4-7 finish the last tile (its buffer is no longer written)
+    if (!lead && active) spv(nt - 1);
     wait_loads<0>();
   };
   int* misc = (int*)(lds + C::MISC_OFF);
