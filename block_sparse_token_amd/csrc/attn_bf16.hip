@@ -719,13 +719,21 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     load_q<C>(a, ((long)(sg.q0 + i) * a.Hq + g * G + hh) * C::D, rvalid, qpos, qf);
     const int u_end = sg.c + i_last + 1;
     const int u_lo = window_start(a, sg, a.positions[sg.q0 + i_first], lds, C::MISC_OFF);
+    const int full_limit = sg.c + i_first;
+    const int pos_last = a.positions[sg.q0 + i_last];
+    // masks only on tiles that some row of the pass does not see in full
+    auto mask_if_needed = [&](const int* kpos, int u0, f32x16 (&sacc)[2]) {
+      const bool full =
+          (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
+      if (!full) apply_mask(kpos, qpos, window, sacc);
+    };
     // sweep 1: row max and normaliser over all visible keys
     float m = kNegBig, lsum = 0.f;
     sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
              [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
       qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
-      apply_mask(kpos, qpos, window, sacc);
+      mask_if_needed(kpos, u0, sacc);
       float mx = kNegBig;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -739,12 +747,13 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rs += __builtin_amdgcn_exp2f(sacc[mb][e] * sl2 - mnew * sl2);
+        for (int e = 0; e < 16; ++e) rs += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -mnew * sl2));
       lsum = lsum * alpha + rs;
     });
     const float lt = pair_sum(lsum);
-    const float inv = rvalid ? 1.f / lt : 0.f;
-    const float mb2 = m * sl2;
+    // p = exp2(s * sl2 - m * sl2) / lt with the division folded into the
+    // exponent; rows past the pass get p = 0
+    const float mb2 = rvalid ? m * sl2 + __log2f(lt) : INFINITY;
     // sweep 2: own keys in 64-key tiles from the segment start.  The first
     // pass (the one holding the segment's last row) writes every block.
     const int first_pass = ps == passes - 1;
@@ -754,18 +763,23 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
              [&](const char* buf, const int* kpos, int u0) {
       f32x16 sacc[2];
       qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
-      apply_mask(kpos, qpos, window, sacc);
+      mask_if_needed(kpos, u0, sacc);
+      // a lane's keys come in runs of four consecutive keys (one 4-aligned
+      // run per S^T register quadruple), and blocks are >= 16 keys, so each
+      // run lies in one block: sum the run, then add it to its block
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(sacc[mb][e] * sl2 - mb2) * inv;
-          const int kk = mb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-          const int bt = B >= 64 ? 0 : kk / B;
+        for (int jg = 0; jg < 4; ++jg) {
+          float s4 = 0.f;
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b == bt) part[b] += p;
+          for (int e = 0; e < 4; ++e)
+            s4 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][jg * 4 + e], sl2, -mb2));
+          const int kk0 = mb * 32 + jg * 8 + h * 4;
+          const int bt = B >= 64 ? 0 : kk0 / B;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) part[b] += b == bt ? s4 : 0.f;
         }
       // reduce over lanes holding rows of the same head (lane % G)
 #pragma unroll
