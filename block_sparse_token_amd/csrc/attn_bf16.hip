@@ -80,7 +80,7 @@ struct Cfg {
   static constexpr int RING_BYTES = 2 * BN * 4;
   static constexpr int RED_OFF = RING_OFF + NRING * RING_BYTES;
   static constexpr int RED_BYTES = NW * 4 * 32 * 4;  // [wave][block in tile][head] f32
-  static constexpr int MISC_OFF = RED_OFF + RED_BYTES;
+  static constexpr int MISC_OFF = RED_OFF + 2 * RED_BYTES;  // two of them, alternating by tile
   static constexpr int LDS_BYTES = MISC_OFF + 64;
   // copies one wave issues per tile step: two index copies, K and V rows
   static constexpr int COPIES_IDX = 2;
@@ -759,47 +759,18 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
     const int first_pass = ps == passes - 1;
     int mt0 = 0;
     if (!first_pass && u_lo > sg.c) mt0 = (u_lo - sg.c) / C::BN;
-    sweep<C>(a, sg, g, sg.c + mt0 * C::BN, u_end, lds,
-             [&](const char* buf, const int* kpos, int u0) {
-      f32x16 sacc[2];
-      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
-      mask_if_needed(kpos, u0, sacc);
-      // a lane's keys come in runs of four consecutive keys (one 4-aligned
-      // run per S^T register quadruple), and blocks are >= 16 keys, so each
-      // run lies in one block: sum the run, then add it to its block
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          float s4 = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s4 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][jg * 4 + e], sl2, -mb2));
-          const int kk0 = mb * 32 + jg * 8 + h * 4;
-          const int bt = B >= 64 ? 0 : kk0 / B;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) part[b] += b == bt ? s4 : 0.f;
-        }
-      // reduce over lanes holding rows of the same head (lane % G)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float x = part[b];
-        x = pair_sum(x);
-        for (int o = 16; o >= G; o >>= 1) x += __shfl_xor(x, o, 64);
-        part[b] = x;
-      }
-      if (l < G) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) red[(w * 4 + b) * 32 + l] = part[b];
-      }
-      lds_barrier();
+    // Per tile: this wave's per-(block, head) sums go to one of two LDS
+    // areas; the sum over waves of a tile is taken in the next tile's body
+    // (after the barrier that ends the step) and that of the last tile after
+    // the sweep, so the sweep needs no barrier of its own.
+    auto finish_tile = [&](int tt, int u0t) {
       if (tid < nbt * G) {
+        const float* rr = red + (tt & 1) * (C::RED_BYTES / 4);
         const int bt = tid / G, h2 = tid % G;
         float tot = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < C::NW; ++ww) tot += red[(ww * 4 + bt) * 32 + h2];
-        const int mt = (u0 - sg.c) / C::BN;
+        for (int ww = 0; ww < C::NW; ++ww) tot += rr[(ww * 4 + bt) * 32 + h2];
+        const int mt = (u0t - sg.c) / C::BN;
         const int kb = (mt * C::BN) / B + bt;
         if (kb < nb) {
           float* dst = a.block_mass + (mbase + kb) * a.Hq + g * G + h2;
@@ -807,7 +778,54 @@ __device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
           else *dst += tot;
         }
       }
+    };
+    const int s2_t0 = sg.c + mt0 * C::BN;
+    sweep<C>(a, sg, g, s2_t0, u_end, lds,
+             [&](const char* buf, const int* kpos, int u0) {
+      f32x16 sacc[2];
+      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
+      mask_if_needed(kpos, u0, sacc);
+      const int tt = (u0 - s2_t0) / C::BN;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      if (B >= C::BN) {
+        // the tile lies in one block
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            part[0] += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -mb2));
+      } else {
+        // a lane's keys come in runs of four consecutive keys (one 4-aligned
+        // run per S^T register quadruple), and blocks are >= 16 keys, so
+        // each run lies in one block: sum the run, then add it to its block
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int jg = 0; jg < 4; ++jg) {
+            float s4 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              s4 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][jg * 4 + e], sl2, -mb2));
+            const int bt = (mb * 32 + jg * 8 + h * 4) / B;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) part[b] += b == bt ? s4 : 0.f;
+          }
+      }
+      // reduce over lanes holding rows of the same head (lane % G)
+      float* rr = red + (tt & 1) * (C::RED_BYTES / 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < nbt) {
+          float x = pair_sum(part[b]);
+          for (int o = 16; o >= G; o >>= 1) x += __shfl_xor(x, o, 64);
+          if (l < G) rr[(w * 4 + b) * 32 + l] = x;
+        }
+      }
+      if (tt > 0) finish_tile(tt - 1, u0 - C::BN);
     });
+    const int nt2 = (u_end - s2_t0 + C::BN - 1) / C::BN;
+    lds_barrier();
+    finish_tile(nt2 - 1, s2_t0 + (nt2 - 1) * C::BN);
   }
 }
 
