@@ -59,7 +59,7 @@ def lib():
             "up_last_error": (ctypes.c_char_p, []),
             "up_version": (ctypes.c_char_p, []),
             "up_block_offsets": (c_i32, [bp, c_i32, c_vp, c_vp]),
-            "up_attn_workspace_bytes": (c_size, [bp, c_i32, c_i32, c_i32, c_i32]),
+            "up_attn_workspace_bytes": (c_size, [bp, c_i32, c_i32, c_i32, c_i32, c_i32]),
             "up_prefill_attn": (c_i32, [bp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_f32, c_i32, c_f32, c_vp, c_i32, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_size, c_vp]),
@@ -145,8 +145,9 @@ def up_block_offsets(batch: Batch, block_size: int, cu_blocks, stream=None):
            "up_block_offsets")
 
 
-def up_attn_workspace_bytes(batch: Batch, dtype, Hq, Hkv, D) -> int:
-    return int(lib().up_attn_workspace_bytes(batch.ref, _DT[dtype], Hq, Hkv, D))
+def up_attn_workspace_bytes(batch: Batch, dtype, Hq, Hkv, D, block_size=0) -> int:
+    """``block_size``: the scoring block size when scores are asked for, else 0."""
+    return int(lib().up_attn_workspace_bytes(batch.ref, _DT[dtype], Hq, Hkv, D, int(block_size)))
 
 
 def up_prefill_attn(batch: Batch, q, k, v, k_cache, v_cache, out, workspace, *, rope_theta=0.0,

@@ -145,14 +145,32 @@ up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* c
                        "block offsets launch");
 }
 
+namespace {
+// bf16 scoring scratch: runs of min(block, 64) keys of every block, one
+// value per last-block row and head, plus one total per last-block row and
+// head of every segment
+size_t score_runs(const up_batch* b, int block_size) {
+  const size_t nb_cap = (size_t)(b->num_tokens + block_size - 1) / block_size + b->num_seqs;
+  return nb_cap * (size_t)(block_size / (block_size < 64 ? block_size : 64));
+}
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
 size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
-                               int32_t D) {
+                               int32_t D, int32_t block_size) {
   if (!batch || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 0;
   const int G = Hq / Hkv;
   if (G > 32) return 0;
   const int P = positions_per_tile(dtype, D, G);
   if (P <= 0) return 0;
-  return 16 + sizeof(int2) * up::work_capacity(batch->num_tokens, batch->num_seqs, P);
+  size_t bytes = 16 + sizeof(int2) * up::work_capacity(batch->num_tokens, batch->num_seqs, P);
+  if (dtype == UP_BF16 && block_size != 0) {
+    if (!valid_block_size(block_size)) return 0;
+    bytes = align256(bytes);
+    bytes += sizeof(float) * score_runs(batch, block_size) * block_size * Hq;
+    bytes += sizeof(float) * (size_t)batch->num_seqs * block_size * Hq;
+  }
+  return bytes;
 }
 
 up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
@@ -186,7 +204,8 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   if (batch->num_seqs > up::kMaxSeqsPlan)
     return fail(UP_ERR_UNSUPPORTED, "at most %d segments per call (got %d)", up::kMaxSeqsPlan,
                 batch->num_seqs);
-  const size_t need = up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D);
+  const size_t need =
+      up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D, score_flags ? block_size : 0);
   if (workspace_bytes < need)
     return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
 
@@ -224,8 +243,9 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
 
   int32_t* count = (int32_t*)workspace;
   int2* items = (int2*)((char*)workspace + 16);
-  e = up::launch_plan(batch->cu_seqlens, batch->ctx_lens, score_flags, batch->num_seqs, P, window,
-                      items, count, cap, s);
+  // the bf16 kernel scores inside its attention items: no score items
+  e = up::launch_plan(batch->cu_seqlens, batch->ctx_lens, bf16 ? nullptr : score_flags,
+                      batch->num_seqs, P, window, items, count, cap, s);
   if (e != hipSuccess) return device_status(e, "work-plan launch");
 
   up::AttnArgs a;
@@ -242,6 +262,12 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   a.score_flags = score_flags;
   a.cu_blocks = cu_blocks;
   a.block_mass = block_mass;
+  a.score_part = nullptr;
+  a.score_lse = nullptr;
+  if (bf16 && score_flags) {
+    a.score_part = (float*)((char*)workspace + align256(16 + sizeof(int2) * (size_t)cap));
+    a.score_lse = a.score_part + score_runs(batch, block_size) * block_size * Hq;
+  }
   a.items = items;
   a.item_count = count;
   a.Hq = Hq;
@@ -263,6 +289,10 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   if (g_attn_ev[1]) {
     e = hipEventRecord(g_attn_ev[1], s);
     if (e != hipSuccess) return device_status(e, "profiling event record");
+  }
+  if (bf16 && score_flags) {
+    e = up::launch_block_mass(a, batch->num_seqs, s);
+    if (e != hipSuccess) return device_status(e, "block mass launch");
   }
   return UP_OK;
 }

@@ -31,11 +31,12 @@
 //    computes no row max and never rescales O.  A tile whose probabilities
 //    pass 2^64 sends the item through a second loop with a running max that
 //    is raised (and O, l rescaled) when a tile's max is 2^8 above it.
-//  * Score items: for a scored segment and KV head, a first QK^T sweep over
-//    every visible key gives the exact softmax normaliser of the rows of the
-//    segment's last query block; a second sweep over the segment's own keys
-//    sums those probabilities per key block.  The result is written to
-//    block_mass[block, head] in a fixed order (deterministic).
+//  * Block importance of a scored segment: the items holding the rows of
+//    its last block store, per row and head, the log2-sum-exp of every run
+//    of min(block, 64) own keys and the row's total log2-sum-exp (key tiles
+//    are aligned to the segment's first own key, so runs never straddle a
+//    tile); block_mass_kernel then sums exp2(run - total) over the rows and
+//    runs of each block in a fixed order (deterministic).
 #include <type_traits>
 
 #include "common.h"
@@ -78,9 +79,7 @@ struct Cfg {
   // ring slot: [0, 256) cache-row source value per key, [256, 512) position
   static constexpr int RING_OFF = NBUF * BUF_BYTES;
   static constexpr int RING_BYTES = 2 * BN * 4;
-  static constexpr int RED_OFF = RING_OFF + NRING * RING_BYTES;
-  static constexpr int RED_BYTES = NW * 4 * 32 * 4;  // [wave][block in tile][head] f32
-  static constexpr int MISC_OFF = RED_OFF + 2 * RED_BYTES;  // two of them, alternating by tile
+  static constexpr int MISC_OFF = RING_OFF + NRING * RING_BYTES;
   static constexpr int LDS_BYTES = MISC_OFF + 64;
   // copies one wave issues per tile step: two index copies, K and V rows
   static constexpr int COPIES_IDX = 2;
@@ -180,7 +179,7 @@ __device__ __forceinline__ void lds_barrier() {
 // ----------------------------------------------------------------------------
 // tile staging
 // ----------------------------------------------------------------------------
-// Keys past the visible range are clamped to the last visible one (real,
+// Keys outside [0, u_end) are clamped to the nearest key in it (real,
 // finite data) and get position INT_MAX, so the mask removes them; every
 // copy reads inside its array and no branch depends on per-key data.
 template <class C>
@@ -201,7 +200,7 @@ struct Stager {
   __device__ inline void index(int k) const {
     if (w != 0) return;
     const int u = t0 + k * C::BN + lane;
-    const int uu = min(u, u_end - 1);
+    const int uu = max(min(u, u_end - 1), 0);
     const bool cached = uu < sg.c;
     const int own = max(uu - sg.c, 0);
     // the source is selected arithmetically (a select of two kernel-argument
@@ -232,7 +231,7 @@ struct Stager {
     for (int x = 0; x < C::WPW; ++x) {
       const int rbase = w * C::KPW + x * C::RPW;
       const int r = rbase + lane / C::CPR;
-      const int uu = min(u0 + r, u_end - 1);
+      const int uu = max(min(u0 + r, u_end - 1), 0);
       const bool cached = uu < sg.c;
       const int page = cached ? val[x] : (val[x] >> 4);
       const int off = cached ? (uu & 15) : (val[x] & 15);
@@ -244,13 +243,14 @@ struct Stager {
       copy16((uintptr_t)a.v_cache + rowb + (pc ^ swv<C::D>(r)) * 16,
              dst + C::V_OFF + rbase * C::RBYTES);
     }
-    // positions: a cached key's is its index, one past the visible range
-    // gets INT_MAX; an own key keeps the copied one (no write)
+    // positions: a cached key's is its index, one outside the key range
+    // (past the visible end, or before key 0) gets INT_MAX; an own key
+    // keeps the copied one (no write)
 #pragma unroll
     for (int x = 0; x < C::WPW; ++x) {
       const int r = w * C::KPW + x * C::RPW + lane / C::CPR;
       const int u = u0 + r;
-      if (pc == 0 && (u >= u_end || u < sg.c)) rp[r] = u < u_end ? u : kPosInvalid;
+      if (pc == 0 && (u >= u_end || u < sg.c)) rp[r] = (u < u_end && u >= 0) ? u : kPosInvalid;
     }
   }
 };
@@ -272,21 +272,16 @@ __device__ inline void sweep_prologue(const Stager<C>& st) {
   wait_loads<C::COPIES_DATA>();  // tile 0 has landed
   lds_barrier();
 }
+// Only tiles that exist are copied: step t issues the index copies of tile
+// t+IA and the data copies of tile t+LA only while those are below nt, and
+// waits for everything but what it issued.
 template <class C>
-__device__ inline void sweep_issue(const Stager<C>& st, int t) {
-  st.index(t + C::IA);
-  st.data(t + C::LA);
-}
-// Attention items copy only tiles that exist: step t issues the index
-// copies of tile t+IA and the data copies of tile t+LA only while those are
-// below nt, and waits for everything but what it issued.
-template <class C>
-__device__ inline void sweep_issue_bounded(const Stager<C>& st, int t, int nt) {
+__device__ inline void sweep_issue(const Stager<C>& st, int t, int nt) {
   if (t + C::IA < nt) st.index(t + C::IA);
   if (t + C::LA < nt) st.data(t + C::LA);
 }
 template <class C>
-__device__ inline void sweep_step_end_bounded(int t, int nt) {
+__device__ inline void sweep_step_end(int t, int nt) {
   const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
   if (t + C::IA < nt) {
     if (w0) wait_loads<C::COPIES_STEP>();
@@ -297,33 +292,6 @@ __device__ inline void sweep_step_end_bounded(int t, int nt) {
     wait_loads<0>();
   }
   lds_barrier();
-}
-template <class C>
-__device__ inline void sweep_step_end() {
-  // everything but this step's copies (wave 0 also issued the index copies):
-  // tile t+1 has landed
-  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0) wait_loads<C::COPIES_STEP>();
-  else wait_loads<C::COPIES_DATA>();
-  lds_barrier();
-}
-
-// Runs body(buf, kpos, u0) over the tiles; buf holds the tile's K and V,
-// kpos its 64 key positions.
-template <class C, class Body>
-__device__ inline void sweep(const AttnArgs& a, const Seg& sg, int g, int t0, int u_end,
-                             char* lds, Body&& body) {
-  const int nt = (u_end - t0 + C::BN - 1) / C::BN;
-  if (nt <= 0) return;
-  const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
-                     (int)(threadIdx.x & 63), lds, lds_addr(lds)};
-  sweep_prologue(st);
-  for (int t = 0; t < nt; ++t) {
-    sweep_issue(st, t);
-    body((const char*)(lds + st.buf_off(t)), (const int*)(lds + st.ring_off(t) + C::BN * 4),
-         t0 + t * C::BN);
-    sweep_step_end<C>();
-  }
-  wait_loads<0>();
 }
 
 // ----------------------------------------------------------------------------
@@ -530,8 +498,28 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   float ms, lsum;   // reference or running max (log2 units), partial row sum
   f32x16 sacc[2];   // S^T of the tile between QK and softmax
 
-  const int t0 = (u_lo / C::BN) * C::BN;
+  // Key tiles are aligned to the segment's first own key (key index c), so
+  // every 16-key step of a tile covers one run of 16 own keys; the first
+  // tile may start before key 0 (those keys are masked).
+  const int t0 = u_lo >= sg.c ? sg.c + ((u_lo - sg.c) / C::BN) * C::BN
+                              : sg.c - ((sg.c - u_lo + C::BN - 1) / C::BN) * C::BN;
   const int nt = (u_end - t0 + C::BN - 1) / C::BN;
+
+  // Block importance (scored segments): the rows of the segment's last
+  // block store, per row and head, the log2-sum-exp of each run of Qs own
+  // keys (Qs = min(block, 64)) and their total log2-sum-exp; mass of block
+  // b = sum over those rows of exp2(run - total) over b's runs
+  // (block_mass_kernel).
+  const int Bs = a.block_size;
+  const bool scored = a.score_flags != nullptr && a.score_flags[s] != 0;
+  const int nbs = scored ? (sg.n + Bs - 1) / Bs : 0;
+  const int r0s = scored ? (nbs - 1) * Bs : 0;
+  const bool item_scores = scored && i_last >= r0s;       // same in every lane
+  const bool row_scores = item_scores && rvalid && i >= r0s && h == 0;
+  const int Qs = scored ? min(Bs, C::BN) : C::BN;
+  const int run_base = scored ? a.cu_blocks[s] * (Bs / Qs) : 0;
+  float* run_lse = row_scores ? a.score_part + (long)(i - r0s) * a.Hq + g * G + hh : nullptr;
+  const long run_stride = (long)Bs * a.Hq;  // between consecutive runs
   const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(w),
                      l, lds, lds_addr(lds)};
 
@@ -543,12 +531,16 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
     const int* kpos = (const int*)(lds + st.ring_off(t) + C::BN * 4);
     qk_tile<C>(tf, qf, sacc);
     const int u0 = t0 + t * C::BN;
-    const bool full =
-        (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
+    const bool full = u0 >= 0 && (u0 + C::BN - 1 <= full_limit) &&
+                      (window <= 0 || kpos[0] > pos_last - window);
     if (!full) apply_mask(kpos, qpos, window, sacc);
   };
   // probabilities of S^T (tile t) against ms, their row sum, O^T += V^T P^T
-  auto probs_pv = [&](int t) {
+  // sc: std::true_type in the loop instances that score (items holding a
+  // scored segment's last-block rows, and the rescaling loop); the others
+  // carry none of that code
+  auto probs_pv = [&](int t, auto sc) {
+    constexpr bool SC = decltype(sc)::value;
     const TileFrag<C> tf(fo, l0 + st.buf_off(t));
     bf16x8 pf[4];
 #pragma unroll
@@ -557,16 +549,31 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       for (int e = 0; e < 16; ++e)
         pf[mb * 2 + (e >> 3)][e & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -ms));
     // row sum of the bf16 probabilities the PV product uses, two per dot2
+    // (per 16-key step where runs are scored)
     const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float rs0 = 0.f, rs1 = 0.f;
+    float rk[4];
+    float rs;
+    if constexpr (SC) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][0], pf[ks][1]}, one2, rs0, false);
-      rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2], pf[ks][3]}, one2, rs1, false);
-      rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][4], pf[ks][5]}, one2, rs0, false);
-      rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, rs1, false);
+      for (int ks = 0; ks < 4; ++ks) {
+        float x0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][0], pf[ks][1]}, one2, 0.f, false);
+        float x1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2], pf[ks][3]}, one2, 0.f, false);
+        x0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][4], pf[ks][5]}, one2, x0, false);
+        x1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, x1, false);
+        rk[ks] = x0 + x1;
+      }
+      rs = (rk[0] + rk[1]) + (rk[2] + rk[3]);
+    } else {
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][0], pf[ks][1]}, one2, rs0, false);
+        rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][2], pf[ks][3]}, one2, rs1, false);
+        rs0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][4], pf[ks][5]}, one2, rs0, false);
+        rs1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[ks][6], pf[ks][7]}, one2, rs1, false);
+      }
+      rs = rs0 + rs1;
     }
-    const float rs = rs0 + rs1;
     lsum += rs;
     // 16-key step ks uses S^T registers (ks%2)*8.. of half ks/2.  V^T
     // fragment of lane l (d = l%32, h = l/32): keys ks*16 + h*4 + 0..3 and
@@ -584,6 +591,23 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
     }
+    // scored segment, last block's rows, own-key tile: the log2-sum-exp of
+    // each run of Qs own keys (after the products, so the branch does not
+    // split the softmax and PV work)
+    const int u0 = t0 + t * C::BN;
+    if (SC && item_scores && u0 >= sg.c) {
+      const int own0 = u0 - sg.c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = Qs == 16 ? j : Qs == 32 ? (j >> 1) : 0;
+        const bool head = Qs == 16 || (Qs == 32 && (j & 1) == 0) || (Qs == 64 && j == 0);
+        if (!head) continue;
+        const float part = Qs == 16 ? rk[j] : Qs == 32 ? rk[j] + rk[j + 1] : rs;
+        const float x = pair_sum(part);
+        if (row_scores && own0 + q * Qs < sg.n)
+          run_lse[(long)(run_base + own0 / Qs + q) * run_stride] = ms + __log2f(x);
+      }
+    }
     return rs;
   };
   // Fast path (reference max): a row's reference is its max over its first
@@ -594,12 +618,12 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   // normalises.  A tile whose row sum passes 2^64 marks the item, which is
   // then recomputed by the rescaling path.
   bool bad = false;
-  auto softmax_pv_ref = [&](int t) {
+  auto softmax_pv_ref = [&](int t, auto sc) {
     if (__any(ms <= kRefUnset)) {
       const float mx = scaled_row_max(sacc, sl2);
       ms = ms > kRefUnset ? ms : fmaxf(ms, mx);
     }
-    const float rs = probs_pv(t);
+    const float rs = probs_pv(t, sc);
     bad = bad || !(rs <= kRefMaxSum);
   };
   // Rescaling path: the running max is raised (and O, l rescaled) when a
@@ -616,7 +640,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       ms = mnew;
     }
-    probs_pv(t);
+    probs_pv(t, std::true_type{});
   };
 
   // The two waves that share a SIMD (w and w+4) work on different stages:
@@ -628,7 +652,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   // A wave whose rows all lie past the item's last token (short segments,
   // decodes) only stages and synchronises.
   const bool active = __any(rvalid);
-  auto run = [&](auto rescale) {
+  auto run = [&](auto rescale, auto sc) {
     constexpr bool R = decltype(rescale)::value;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -638,7 +662,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
     lsum = 0.f;
     auto spv = [&](int t) {
       if constexpr (R) softmax_pv_rescale(t);
-      else softmax_pv_ref(t);
+      else softmax_pv_ref(t, sc);
     };
     sweep_prologue(st);
     for (int t = 0; t < nt; ++t) {
@@ -646,14 +670,14 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
       // the step, so the copies of a step never all queue at once
       if (lead) {
         if (active) qk(t);
-        sweep_issue_bounded(st, t, nt);
+        sweep_issue(st, t, nt);
         if (active) spv(t);
       } else {
         if (t > 0 && active) spv(t - 1);
         if (active) qk(t);
-        sweep_issue_bounded(st, t, nt);
+        sweep_issue(st, t, nt);
       }
-      sweep_step_end_bounded<C>(t, nt);
+      sweep_step_end<C>(t, nt);
     }
     // waves 4-7 finish the last tile (its buffer is no longer written)
     if (!lead && active) spv(nt - 1);
@@ -661,13 +685,20 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   };
   int* misc = (int*)(lds + C::MISC_OFF);
   if (tid == 0) misc[1] = 0;  // published by the prologue's barriers
-  run(std::false_type{});
+  if (item_scores) run(std::false_type{}, std::true_type{});
+  else run(std::false_type{}, std::false_type{});
   if (__any(bad) && l == 0) misc[1] = 1;
   lds_barrier();
-  if (misc[1]) run(std::true_type{});
+  if (misc[1]) run(std::true_type{}, std::true_type{});
 
   // epilogue: normalise and store; lane holds d = db*32 + jg*8 + h*4 + e
   const float ltot = pair_sum(lsum);
+  if (row_scores) {
+    a.score_lse[((long)s * Bs + (i - r0s)) * a.Hq + g * G + hh] = ms + __log2f(ltot);
+    // runs before the first tile (outside the window of every row here)
+    for (int q = 0; q < (t0 - sg.c) / Qs; ++q)
+      run_lse[(long)(run_base + q) * run_stride] = -INFINITY;
+  }
   if (!rvalid) return;
   uint16_t* out = (uint16_t*)a.out;
   const float inv = 1.f / ltot;
@@ -683,152 +714,6 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   if (a.lse && h == 0) a.lse[qrow / C::D] = (ms + __log2f(ltot)) * 0.69314718055994530942f;
 }
 
-// ----------------------------------------------------------------------------
-// score item: block mass of the last query block of segment s, KV head g
-// ----------------------------------------------------------------------------
-template <class C>
-__device__ void score_item(const AttnArgs& a, int s, int g, char* lds) {
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, h = l >> 5;
-  Seg sg;
-  sg.s = s;
-  sg.q0 = a.cu_seqlens[s];
-  sg.n = a.cu_seqlens[s + 1] - sg.q0;
-  sg.c = a.ctx_lens[s];
-  const int G = a.G, B = a.block_size;
-  const int nb = (sg.n + B - 1) / B;
-  const int r0 = (nb - 1) * B;
-  const int rows_total = (sg.n - r0) * G;
-  const int passes = (rows_total + C::ROWS - 1) / C::ROWS;
-  const long mbase = (long)a.cu_blocks[s];
-  const float sl2 = a.scale_log2;
-  const int window = a.window;
-  float* red = (float*)(lds + C::RED_OFF);
-  const int nbt = B >= 64 ? 1 : 64 / B;  // blocks per 64-key tile
-  const FragOffsets<C> fo;
-
-  for (int ps = passes - 1; ps >= 0; --ps) {
-    const int rbeg = ps * C::ROWS;
-    const int rend = min(rows_total, rbeg + C::ROWS);
-    const int i_first = r0 + rbeg / G;
-    const int i_last = r0 + (rend - 1) / G;
-    const int r = rbeg + w * 32 + (l & 31);
-    const int i = r0 + r / G, hh = r % G;
-    const bool rvalid = r < rend;
-    const int qpos = rvalid ? a.positions[sg.q0 + i] : -1;
-    bf16x8 qf[C::KC];
-    load_q<C>(a, ((long)(sg.q0 + i) * a.Hq + g * G + hh) * C::D, rvalid, qpos, qf);
-    const int u_end = sg.c + i_last + 1;
-    const int u_lo = window_start(a, sg, a.positions[sg.q0 + i_first], lds, C::MISC_OFF);
-    const int full_limit = sg.c + i_first;
-    const int pos_last = a.positions[sg.q0 + i_last];
-    // masks only on tiles that some row of the pass does not see in full
-    auto mask_if_needed = [&](const int* kpos, int u0, f32x16 (&sacc)[2]) {
-      const bool full =
-          (u0 + C::BN - 1 <= full_limit) && (window <= 0 || kpos[0] > pos_last - window);
-      if (!full) apply_mask(kpos, qpos, window, sacc);
-    };
-    // sweep 1: row max and normaliser over all visible keys
-    float m = kNegBig, lsum = 0.f;
-    sweep<C>(a, sg, g, (u_lo / C::BN) * C::BN, u_end, lds,
-             [&](const char* buf, const int* kpos, int u0) {
-      f32x16 sacc[2];
-      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
-      mask_if_needed(kpos, u0, sacc);
-      float mx = kNegBig;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[mb][e]);
-      mx = pair_max(mx);
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * sl2);
-      m = mnew;
-      float rs = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rs += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -mnew * sl2));
-      lsum = lsum * alpha + rs;
-    });
-    const float lt = pair_sum(lsum);
-    // p = exp2(s * sl2 - m * sl2) / lt with the division folded into the
-    // exponent; rows past the pass get p = 0
-    const float mb2 = rvalid ? m * sl2 + __log2f(lt) : INFINITY;
-    // sweep 2: own keys in 64-key tiles from the segment start.  The first
-    // pass (the one holding the segment's last row) writes every block.
-    const int first_pass = ps == passes - 1;
-    int mt0 = 0;
-    if (!first_pass && u_lo > sg.c) mt0 = (u_lo - sg.c) / C::BN;
-    // Per tile: this wave's per-(block, head) sums go to one of two LDS
-    // areas; the sum over waves of a tile is taken in the next tile's body
-    // (after the barrier that ends the step) and that of the last tile after
-    // the sweep, so the sweep needs no barrier of its own.
-    auto finish_tile = [&](int tt, int u0t) {
-      if (tid < nbt * G) {
-        const float* rr = red + (tt & 1) * (C::RED_BYTES / 4);
-        const int bt = tid / G, h2 = tid % G;
-        float tot = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < C::NW; ++ww) tot += rr[(ww * 4 + bt) * 32 + h2];
-        const int mt = (u0t - sg.c) / C::BN;
-        const int kb = (mt * C::BN) / B + bt;
-        if (kb < nb) {
-          float* dst = a.block_mass + (mbase + kb) * a.Hq + g * G + h2;
-          if (first_pass && (B <= C::BN || ((mt * C::BN) % B) == 0)) *dst = tot;
-          else *dst += tot;
-        }
-      }
-    };
-    const int s2_t0 = sg.c + mt0 * C::BN;
-    sweep<C>(a, sg, g, s2_t0, u_end, lds,
-             [&](const char* buf, const int* kpos, int u0) {
-      f32x16 sacc[2];
-      qk_tile<C>(TileFrag<C>(fo, lds_addr(buf)), qf, sacc);
-      mask_if_needed(kpos, u0, sacc);
-      const int tt = (u0 - s2_t0) / C::BN;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-      if (B >= C::BN) {
-        // the tile lies in one block
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            part[0] += __builtin_amdgcn_exp2f(fmaf(sacc[mb][e], sl2, -mb2));
-      } else {
-        // a lane's keys come in runs of four consecutive keys (one 4-aligned
-        // run per S^T register quadruple), and blocks are >= 16 keys, so
-        // each run lies in one block: sum the run, then add it to its block
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int jg = 0; jg < 4; ++jg) {
-            float s4 = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              s4 += __builtin_amdgcn_exp2f(fmaf(sacc[mb][jg * 4 + e], sl2, -mb2));
-            const int bt = (mb * 32 + jg * 8 + h * 4) / B;
-#pragma unroll
-            for (int b = 0; b < 4; ++b) part[b] += b == bt ? s4 : 0.f;
-          }
-      }
-      // reduce over lanes holding rows of the same head (lane % G)
-      float* rr = red + (tt & 1) * (C::RED_BYTES / 4);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < nbt) {
-          float x = pair_sum(part[b]);
-          for (int o = 16; o >= G; o >>= 1) x += __shfl_xor(x, o, 64);
-          if (l < G) rr[(w * 4 + b) * 32 + l] = x;
-        }
-      }
-      if (tt > 0) finish_tile(tt - 1, u0 - C::BN);
-    });
-    const int nt2 = (u_end - s2_t0 + C::BN - 1) / C::BN;
-    lds_barrier();
-    finish_tile(nt2 - 1, s2_t0 + (nt2 - 1) * C::BN);
-  }
-}
-
 template <int D>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -837,8 +722,42 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const int g = blockIdx.x % a.Hkv;
   if (item >= *a.item_count) return;
   const int2 it = a.items[item];
-  if (it.y == kScoreTile) score_item<C>(a, it.x, g, lds);
-  else attn_item<C>(a, it.x, it.y, g, lds);
+  attn_item<C>(a, it.x, it.y, g, lds);
+}
+
+// Block mass of every scored segment from the run and row log2-sum-exps
+// the attention items stored: one workgroup per segment, one thread per
+// (block, head); runs that start after a row's own position are not read
+// (they hold no visible key and were not all written).
+__global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restrict__ cu_seqlens,
+                                                         const uint8_t* __restrict__ score_flags,
+                                                         const int32_t* __restrict__ cu_blocks,
+                                                         const float* __restrict__ score_part,
+                                                         const float* __restrict__ score_lse,
+                                                         int Hq, int B, float* __restrict__ mass) {
+  const int s = blockIdx.x;
+  if (!score_flags[s]) return;
+  const int n = cu_seqlens[s + 1] - cu_seqlens[s];
+  const int nb = (n + B - 1) / B;
+  const int r0 = (nb - 1) * B, rows = n - r0;
+  const int Q = min(B, 64), rpb = B / Q;
+  const long run_base = (long)cu_blocks[s] * rpb;
+  for (int idx = threadIdx.x; idx < nb * Hq; idx += 256) {
+    const int b = idx / Hq, h = idx % Hq;
+    float m = 0.f;
+    for (int rl = 0; rl < rows; ++rl) {
+      const float tot = score_lse[((long)s * B + rl) * Hq + h];
+      for (int j = 0; j < rpb && b * B + j * Q <= r0 + rl; ++j)
+        m += exp2f(score_part[((run_base + b * rpb + j) * B + rl) * Hq + h] - tot);
+    }
+    mass[((long)cu_blocks[s] + b) * Hq + h] = m;
+  }
+}
+
+hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st) {
+  hipLaunchKernelGGL(block_mass_kernel, dim3(S), dim3(256), 0, st, a.cu_seqlens, a.score_flags,
+                     a.cu_blocks, a.score_part, a.score_lse, a.Hq, a.block_size, a.block_mass);
+  return hipGetLastError();
 }
 
 int attn_bf16_positions_per_tile(int D, int G) {

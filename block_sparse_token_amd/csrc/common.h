@@ -40,6 +40,10 @@ struct AttnArgs {
   const uint8_t* score_flags;
   const int32_t* cu_blocks;
   float* block_mass;
+  // bf16 path, scored segments: run and row log2-sum-exps of the last
+  // block's rows (score_part [runs][block][Hq], score_lse [S][block][Hq])
+  float* score_part;
+  float* score_lse;
   const int2* items;
   const int32_t* item_count;
   int Hq, Hkv, G, max_pages, block_size, window, rope;
@@ -76,6 +80,7 @@ hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens
                               const int32_t* positions, const int32_t* slot_mapping,
                               const int32_t* block_table, int S, int T, int max_pages,
                               int num_pages, int32_t* err, hipStream_t st);
+hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st);
 hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,

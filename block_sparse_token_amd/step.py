@@ -75,7 +75,8 @@ class PrefillCall:
         self.cu_blocks = torch.empty(S + 1, dtype=torch.int32, device=dev)
         scoring = self.flags is not None
         self.block_mass = torch.empty(NB * Hq, dtype=torch.float32, device=dev) if scoring else None
-        nbytes = B.up_attn_workspace_bytes(self.batch, self.q.dtype, Hq, self.k.shape[1], D)
+        nbytes = B.up_attn_workspace_bytes(self.batch, self.q.dtype, Hq, self.k.shape[1], D,
+                                           self.block_size if scoring else 0)
         self.attn_ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.scores = torch.empty(NB, dtype=torch.float32, device=dev)
         self.keep = torch.empty(NB, dtype=torch.uint8, device=dev)

@@ -104,11 +104,14 @@ up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* c
                            void* stream);
 
 /*
- * Workspace bytes up_prefill_attn needs for this batch shape (the work list
- * of query tiles and score items).
+ * Workspace bytes up_prefill_attn needs for this batch shape: the work list
+ * of query tiles (and, for UP_F32, score items), plus for UP_BF16 with
+ * scoring the per-row run sums of the segments' last blocks.  block_size:
+ * the block size up_prefill_attn will be called with when it gets
+ * score_flags, else 0.  Returns 0 for an unsupported shape.
  */
 size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
-                               int32_t D);
+                               int32_t D, int32_t block_size);
 
 /*
  * Attention with rotary positions, KV-cache write and fused block mass.

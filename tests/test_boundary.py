@@ -77,7 +77,7 @@ def test_attention_argument_validation(L):
     assert "4096" in L.up_last_error().decode()
     assert _attn(L, b, flags=FAKE, block=48) == UP_ERR_UNSUPPORTED
     assert _attn(L, b, theta=float("nan")) == UP_ERR_INVALID
-    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128)
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128, 0)
     assert need > 16
     assert _attn(L, b, ws_bytes=need - 1) == UP_ERR_WORKSPACE
     assert b"workspace" in L.up_last_error()
@@ -89,9 +89,22 @@ def test_attention_argument_validation(L):
 def test_workspace_size_arithmetic(L):
     b = _batch(S=16, T=70000)
     # bf16: 256 packed rows per tile -> 64 positions at GQA 4; one int2 per item
-    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128)
-    assert need == 16 + 8 * (math.ceil(70000 / 64) + 2 * 16 + 1)
-    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128) == 0
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 0)
+    items = 16 + 8 * (math.ceil(70000 / 64) + 2 * 16 + 1)
+    assert need == items
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128, 0) == 0
+    # scoring in bf16 adds, from a 256-byte boundary, one float per (run of
+    # min(block, 64) keys, last-block row, head) for every possible block,
+    # and one per (segment, last-block row, head)
+    base = -(-items // 256) * 256
+    for B in (16, 64, 128):
+        runs = (math.ceil(70000 / B) + 16) * (B // min(B, 64))
+        want = base + 4 * runs * B * 32 + 4 * 16 * B * 32
+        assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, B) == want, B
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 48) == 0
+    # float32 scores in its own items: no extra space
+    assert (L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 16)
+            == L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 0))
     assert L.up_compact_workspace_bytes(16, 1100) == 8 * (1100 + 4)
     assert L.up_compact_workspace_bytes(16, 0) == 0
 
