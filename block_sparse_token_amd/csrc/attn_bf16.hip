@@ -35,8 +35,8 @@
 //    its last block store, per row and head, the log2-sum-exp of every run
 //    of min(block, 64) own keys and the row's total log2-sum-exp (key tiles
 //    are aligned to the segment's first own key, so runs never straddle a
-//    tile); block_mass_kernel then sums exp2(run - total) over the rows and
-//    runs of each block in a fixed order (deterministic).
+//    tile); block_mass_kernel (mass.hip) then sums exp2(run - total) over
+//    the rows and runs of each block in a fixed order (deterministic).
 #include <type_traits>
 
 #include "common.h"
@@ -723,41 +723,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   if (item >= *a.item_count) return;
   const int2 it = a.items[item];
   attn_item<C>(a, it.x, it.y, g, lds);
-}
-
-// Block mass of every scored segment from the run and row log2-sum-exps
-// the attention items stored: one workgroup per segment, one thread per
-// (block, head); runs that start after a row's own position are not read
-// (they hold no visible key and were not all written).
-__global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restrict__ cu_seqlens,
-                                                         const uint8_t* __restrict__ score_flags,
-                                                         const int32_t* __restrict__ cu_blocks,
-                                                         const float* __restrict__ score_part,
-                                                         const float* __restrict__ score_lse,
-                                                         int Hq, int B, float* __restrict__ mass) {
-  const int s = blockIdx.x;
-  if (!score_flags[s]) return;
-  const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-  const int nb = (n + B - 1) / B;
-  const int r0 = (nb - 1) * B, rows = n - r0;
-  const int Q = min(B, 64), rpb = B / Q;
-  const long run_base = (long)cu_blocks[s] * rpb;
-  for (int idx = threadIdx.x; idx < nb * Hq; idx += 256) {
-    const int b = idx / Hq, h = idx % Hq;
-    float m = 0.f;
-    for (int rl = 0; rl < rows; ++rl) {
-      const float tot = score_lse[((long)s * B + rl) * Hq + h];
-      for (int j = 0; j < rpb && b * B + j * Q <= r0 + rl; ++j)
-        m += exp2f(score_part[((run_base + b * rpb + j) * B + rl) * Hq + h] - tot);
-    }
-    mass[((long)cu_blocks[s] + b) * Hq + h] = m;
-  }
-}
-
-hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st) {
-  hipLaunchKernelGGL(block_mass_kernel, dim3(S), dim3(256), 0, st, a.cu_seqlens, a.score_flags,
-                     a.cu_blocks, a.score_part, a.score_lse, a.Hq, a.block_size, a.block_mass);
-  return hipGetLastError();
 }
 
 int attn_bf16_positions_per_tile(int D, int G) {
