@@ -245,7 +245,7 @@ def traffic_from_profile(src_hash):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m = re.search(r"kernel code sha256: ([0-9a-f]+)", txt)
+    m = re.search(r"kernel code sha256[^:\n]*: ([0-9a-f]{64})", txt)
     t = re.search(r"HBM bytes per launch \(scaled\): ([0-9.eE+]+)", txt)
     if not m or not t or m.group(1) != src_hash:
         return None

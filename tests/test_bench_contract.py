@@ -1,0 +1,40 @@
+"""Host-side parts of bench.py's output contract (no GPU)."""
+import os
+import re
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_counter_summary_is_read_when_its_hash_matches():
+    """The committed HBM counter summary of the attention kernel names the
+    kernel source it was taken on; bench.py reads its byte figure for that
+    source and for no other."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_packed_llama8b_counters.md")
+    txt = open(path).read()
+    hashes = re.findall(r"\b[0-9a-f]{64}\b", txt)
+    assert len(hashes) == 1
+    t = bench.traffic_from_profile(hashes[0])
+    assert t is not None and t > 0
+    assert bench.traffic_from_profile("0" * 64) is None
+
+
+def test_kernel_hash_ignores_comments_and_whitespace(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    a.write_text("int f(int x) { // one\n  return x + 1; /* two */ }\n")
+    b.write_text("int f(int x)\n{\n return x + 1;\n}\n")
+    assert bench.kernel_code_hash(str(a)) == bench.kernel_code_hash(str(b))
+    b.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_code_hash(str(a)) != bench.kernel_code_hash(str(b))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
