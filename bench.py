@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--propagation", action="store_true",
+                    help="time one later layer's linear maps on all vs the kept tokens of the "
+                         "headline batch")
     ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + OTHER_WORKLOADS,
                     help="the headline workload (default) or one of the other parity workloads, "
                          "timed over all of its calls")
@@ -288,6 +291,30 @@ def attainable_peaks(torch, B, stream):
                       "up_peak_copy (1 GiB read + 1 GiB written), medians of event-timed launches"}
 
 
+def headline_call(torch):
+    """The headline workload's one call, staged on the GPU: inputs, caches,
+    batch metadata, and the hidden states, positions and KV slots to compact."""
+    import workloads as W
+    from block_sparse_token_amd import step as ST
+
+    wl = W.make(WORKLOAD)
+    call = wl.calls[0]
+    dev = "cuda"
+    kc = torch.zeros((wl.num_pages, wl.Hkv, W.PAGE_SIZE, wl.D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
+                          call.block_table, device=dev)
+    rows = [("hidden", ST.stored_to_tensor(call.hidden, dev)),
+            ("positions", torch.from_numpy(call.positions.astype(np.int32)).to(dev)),
+            ("slot_mapping", torch.from_numpy(call.slot_mapping.astype(np.int32)).to(dev))]
+    pc = ST.PrefillCall(batch=batch, q=ST.stored_to_tensor(call.q, dev),
+                        k=ST.stored_to_tensor(call.k, dev), v=ST.stored_to_tensor(call.v, dev),
+                        k_cache=kc, v_cache=vc, num_blocks=call.num_blocks(wl.block_size),
+                        flags=torch.from_numpy(call.flags.astype(np.uint8)).to(dev),
+                        block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, rows=rows)
+    return wl, call, pc
+
+
 def cpu_baseline(wl, call, budget_s):
     """Time the oracle on whole prompts of the batch, picked near the
     token-weighted mean length (attention cost per token grows with length),
@@ -324,6 +351,122 @@ def cpu_baseline(wl, call, budget_s):
                       f"compaction, float64 NumPy, {spent:.1f} s"}
 
 
+def run_propagation(args):
+    """Payoff of the selection in the later layers: one Llama-3.1-8B-shaped
+    later layer's linear maps (query/key/value projection 4096 -> 6144,
+    output projection 4096 -> 4096, SwiGLU gate and up projections 4096 ->
+    2 x 14336, down projection 14336 -> 4096; random bf16 weights) run on all
+    tokens of the headline batch and on the tokens its selection kept (the
+    compacted hidden states, with the kept count read on the device).  The
+    output projection takes the hidden states as its input (the attention
+    output of a later layer has the same shape).  Prints one JSON line."""
+    import torch
+    import oracle
+    from block_sparse_token_amd import binding as B
+    from oracle.prefill import default_threads
+
+    wl, call, pc = headline_call(torch)
+    pc.launch()
+    torch.cuda.synchronize()
+    T = call.T
+    kept = int(pc.num_kept.item())
+    H, D = wl.hidden_width, wl.D
+    QKV, MLP = (wl.Hq + 2 * wl.Hkv) * D, 14336
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+
+    def weight(n, k):
+        return (torch.randn((n, k), generator=g, device="cuda") * (k ** -0.5)).to(torch.bfloat16)
+
+    w_qkv, w_o = weight(QKV, H), weight(H, H)
+    w_gate, w_up = weight(MLP, H), weight(MLP, H)
+    w_gu = B.interleave_gate_up(w_gate, w_up)
+    w_down = weight(H, MLP)
+    x_all = dict(pc.rows)["hidden"]
+    x_kept = pc.rows_out["hidden"]
+    qkv = torch.empty((T, QKV), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    hmid = torch.empty((T, MLP), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    maps = [("qkv", H, QKV), ("o", H, H), ("gate_up_swiglu", H, 2 * MLP), ("down", MLP, H)]
+    stream = torch.cuda.current_stream()
+
+    def layer(x, rows_dev, ev=None):
+        args_ = [(x, w_qkv, qkv, B.UP_ACT_NONE), (x, w_o, o, B.UP_ACT_NONE),
+                 (x, w_gu, hmid, B.UP_ACT_SWIGLU), (hmid, w_down, y, B.UP_ACT_NONE)]
+        for j, (inp, w, out, act) in enumerate(args_):
+            if ev is not None:
+                ev[j][0].record(stream)
+            B.up_linear_bf16(inp, w, out, rows_in_use=rows_dev, act=act)
+            if ev is not None:
+                ev[j][1].record(stream)
+
+    def timed(x, rows_dev):
+        for _ in range(args.warmup):
+            layer(x, rows_dev)
+        torch.cuda.synchronize()
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in maps] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for ev in evs:
+            layer(x, rows_dev, ev)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        per_map = [float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for ev in evs]))
+                   for j in range(len(maps))]
+        return wall, per_map
+
+    wall_all, ms_all = timed(x_all, None)
+    wall_kept, ms_kept = timed(x_kept, pc.num_kept)
+    res_maps = {}
+    for j, (name, K, N) in enumerate(maps):
+        f_all, f_kept = 2.0 * T * K * N, 2.0 * kept * K * N
+        res_maps[name] = {"K": K, "N": N, "ms_all": ms_all[j], "ms_kept": ms_kept[j],
+                          "TFLOP/s_all": f_all / (ms_all[j] * 1e-3) / 1e12,
+                          "TFLOP/s_kept": f_kept / (ms_kept[j] * 1e-3) / 1e12,
+                          "frac_all": f_all / (ms_all[j] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    flops_all = oracle.later_layer_flops(T, H, QKV, MLP)
+    flops_kept = oracle.later_layer_flops(kept, H, QKV, MLP)
+    dominant = max(res_maps, key=lambda k: res_maps[k]["ms_all"])
+    dm = res_maps[dominant]
+    res = {
+        "metric": "later-layer linear maps on the kept tokens vs all tokens (ms per layer)",
+        "value": wall_kept, "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "one Llama-3.1-8B-shaped later layer (4096 -> 6144, 4096 -> 4096, "
+                               "SwiGLU 4096 -> 2 x 14336, 14336 -> 4096) on the packed prefill of "
+                               f"{T} tokens, {kept} kept by top-p 0.95 (block 64)",
+                   "rows_all": T, "rows_kept": kept},
+        "layer_ms_all": wall_all, "layer_ms_kept": wall_kept,
+        "time_saved_frac": 1.0 - wall_kept / wall_all,
+        "flops_all": flops_all, "flops_kept": flops_kept,
+        "flops_saved_frac": 1.0 - flops_kept / flops_all,
+        "maps": res_maps,
+        "roofline": {"bound": "mfma", "kernel": "linear_bf16_kernel", "map": dominant,
+                     "achieved": dm["TFLOP/s_all"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dm["frac_all"], "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's four maps on the first kept rows, float64 on this host
+        n = 512
+        xs = x_kept[:n].float().cpu().numpy().astype(np.float64)
+        ws = {k: v.float().cpu().numpy().astype(np.float64)
+              for k, v in (("qkv", w_qkv), ("o", w_o), ("gate", w_gate), ("up", w_up),
+                           ("down", w_down))}
+        t0 = time.perf_counter()
+        oracle.linear(xs, ws["qkv"])
+        oracle.linear(xs, ws["o"])
+        hs = oracle.swiglu(xs, ws["gate"], ws["up"])
+        oracle.linear(hs, ws["down"])
+        spent = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n / spent, "unit": "rows/s", "cores": default_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} kept rows through the four maps, float64 NumPy "
+                                         f"matrix products, {spent:.2f} s",
+                               "gpu_rows_per_s_kept": kept / (wall_kept * 1e-3)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -342,29 +485,16 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
         return
 
+    if args.propagation:
+        run_propagation(args)
+        return
     if args.workload != WORKLOAD:
         run_other_workload(args)
         return
 
-    import workloads as W
     from block_sparse_token_amd import binding as B
-    from block_sparse_token_amd import step as ST
 
-    wl = W.make(WORKLOAD)
-    call = wl.calls[0]
-    dev = "cuda"
-    kc = torch.zeros((wl.num_pages, wl.Hkv, W.PAGE_SIZE, wl.D), dtype=torch.bfloat16, device=dev)
-    vc = torch.zeros_like(kc)
-    batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
-                          call.block_table, device=dev)
-    rows = [("hidden", ST.stored_to_tensor(call.hidden, dev)),
-            ("positions", torch.from_numpy(call.positions.astype(np.int32)).to(dev)),
-            ("slot_mapping", torch.from_numpy(call.slot_mapping.astype(np.int32)).to(dev))]
-    pc = ST.PrefillCall(batch=batch, q=ST.stored_to_tensor(call.q, dev),
-                        k=ST.stored_to_tensor(call.k, dev), v=ST.stored_to_tensor(call.v, dev),
-                        k_cache=kc, v_cache=vc, num_blocks=call.num_blocks(wl.block_size),
-                        flags=torch.from_numpy(call.flags.astype(np.uint8)).to(dev),
-                        block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, rows=rows)
+    wl, call, pc = headline_call(torch)
     stream = torch.cuda.current_stream()
     K, Wm = args.steps, args.warmup
 

@@ -70,6 +70,7 @@ def lib():
             "up_check_batch": (c_i32, [bp, c_i32, c_vp, c_vp]),
             "up_peak_mfma_bf16": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
             "up_peak_copy": (c_i32, [c_vp, c_vp, c_size, c_vp]),
+            "up_linear_bf16": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
         }
@@ -84,7 +85,7 @@ def lib():
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
-            "up_peak_copy"]
+            "up_peak_copy", "up_linear_bf16"]
 
 
 def _check(st: int, what: str):
@@ -224,3 +225,37 @@ def up_peak_copy(src, dst, stream=None):
     if dst.numel() * dst.element_size() < n:
         raise UniprefillError("dst is smaller than src")
     _check(lib().up_peak_copy(_p(src), _p(dst), n, _stream(stream)), "up_peak_copy")
+
+
+UP_ACT_NONE, UP_ACT_SWIGLU = 0, 1
+
+
+def up_linear_bf16(x, w, y, rows_in_use=None, act=UP_ACT_NONE, stream=None):
+    """y = x w^T over the rows in use (``rows_in_use``: a one-element int32
+    device tensor, e.g. the kept count of up_compact; None = all rows of x),
+    or the SwiGLU-gated product with ``act=UP_ACT_SWIGLU`` (w's gate and up
+    rows interleaved in groups of 32).  x [rows, K], w [N, K], y [rows, N]
+    or [rows, N / 2], all bfloat16."""
+    for name, t in (("x", x), ("w", w), ("y", y)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise UniprefillError(f"{name} must be a 2-D bfloat16 tensor")
+    rows, K = x.shape
+    N = w.shape[0]
+    out_cols = N // 2 if act == UP_ACT_SWIGLU else N
+    if w.shape[1] != K or y.shape[0] < rows or y.shape[1] != out_cols:
+        raise UniprefillError(f"shapes do not match: x {tuple(x.shape)}, w {tuple(w.shape)}, "
+                              f"y {tuple(y.shape)}")
+    if rows_in_use is not None and (rows_in_use.dtype != torch.int32 or rows_in_use.numel() < 1):
+        raise UniprefillError("rows_in_use must be an int32 device tensor")
+    _check(lib().up_linear_bf16(_p(x), _p(w), _p(y), rows, _p(rows_in_use), N, K, act,
+                                _stream(stream)), "up_linear_bf16")
+
+
+def interleave_gate_up(w_gate, w_up):
+    """The weight layout UP_ACT_SWIGLU reads: gate and up rows ([F, K] each,
+    F a multiple of 128) interleaved in groups of 32 rows -> [2F, K]."""
+    F, K = w_gate.shape
+    if w_up.shape != (F, K) or F % 128:
+        raise UniprefillError("gate and up weights must share a shape [F, K], F a multiple of 128")
+    return torch.stack([w_gate.reshape(F // 32, 32, K), w_up.reshape(F // 32, 32, K)],
+                       dim=1).reshape(2 * F, K).contiguous()

@@ -133,6 +133,27 @@ up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return device_status(up::launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak copy launch");
 }
 
+up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap,
+                         const int32_t* rows_in_use, int32_t n_out, int32_t k_in, int32_t act,
+                         void* stream) {
+  if (!x || !w || !y) return fail(UP_ERR_INVALID, "x, w and y must be non-NULL");
+  if (rows_cap < 0) return fail(UP_ERR_INVALID, "rows_cap must be >= 0 (got %d)", rows_cap);
+  if (n_out <= 0 || n_out % 256)
+    return fail(UP_ERR_UNSUPPORTED, "n_out must be a positive multiple of 256 (got %d)", n_out);
+  if (k_in <= 0 || k_in % 64)
+    return fail(UP_ERR_UNSUPPORTED, "k_in must be a positive multiple of 64 (got %d)", k_in);
+  if (act != UP_ACT_NONE && act != UP_ACT_SWIGLU)
+    return fail(UP_ERR_INVALID, "act must be UP_ACT_NONE or UP_ACT_SWIGLU (got %d)", act);
+  if ((double)rows_cap * k_in * 2 >= 4294967296.0 || (double)n_out * k_in * 2 >= 4294967296.0)
+    return fail(UP_ERR_UNSUPPORTED, "x and w must each be under 4 GiB (32-bit row offsets)");
+  if ((((uintptr_t)x) | ((uintptr_t)w)) & 15)
+    return fail(UP_ERR_INVALID, "x and w must be 16-byte aligned");
+  if (((uintptr_t)y) & 7) return fail(UP_ERR_INVALID, "y must be 8-byte aligned");
+  return device_status(up::launch_linear_bf16(x, w, y, rows_cap, rows_in_use, n_out, k_in, act,
+                                              as_stream(stream)),
+                       "linear launch");
+}
+
 up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
                            void* stream) {
   up_status st = check_batch(batch, false);

@@ -217,6 +217,32 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Later-layer linear map on the kept tokens (UniPrefill review, Method & Key
+ * Results: dropped tokens skip every later sublayer, so the later layers'
+ * matrix products run on the compacted rows; paper entry, abstract).  bf16
+ * in and out, float32 accumulation:
+ *   act = UP_ACT_NONE:   y[m][n] = sum_k x[m][k] * w[n][k]          y [rows, n_out]
+ *   act = UP_ACT_SWIGLU: y[m][f] = silu(g) * u, g and u the sums for w's
+ *     gate row and up row of feature f (silu(z) = z / (1 + e^-z); the
+ *     SwiGLU gate of Llama-style MLPs, Shazeer 2020)             y [rows, n_out / 2]
+ *     w holds gate and up rows interleaved in groups of 32: rows 64q..64q+31
+ *     are the gate rows of features 32q..32q+31, rows 64q+32..64q+63 their
+ *     up rows.
+ * x: [rows_cap, k_in] row-major bf16, 16-byte aligned; w: [n_out, k_in]
+ * row-major bf16 (the [out, in] layout), 16-byte aligned; y: 8-byte aligned.
+ * rows_in_use (device, may be NULL): rows used = min(*rows_in_use,
+ * rows_cap), e.g. the num_kept that up_compact wrote, so no host
+ * synchronisation is needed; NULL uses rows_cap.  Rows of y at or beyond
+ * the rows used are not written.  n_out: a multiple of 256; k_in: a
+ * multiple of 64; x and w each under 4 GiB (UP_ERR_UNSUPPORTED otherwise).
+ */
+#define UP_ACT_NONE 0
+#define UP_ACT_SWIGLU 1
+up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap,
+                         const int32_t* rows_in_use, int32_t n_out, int32_t k_in, int32_t act,
+                         void* stream);
+
+/*
  * Profiling aid (not part of the operator).  With both arguments non-NULL
  * (hipEvent_t handles created by the caller), up_prefill_attn calls made
  * afterwards on this thread record attn_start on their stream right before

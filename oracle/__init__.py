@@ -15,3 +15,4 @@ from .prefill import (  # noqa: F401
     topp_select,
     visible,
 )
+from .layers import later_layer_flops, linear, silu, swiglu  # noqa: F401

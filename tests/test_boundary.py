@@ -159,3 +159,20 @@ def test_peak_probe_argument_validation(L):
     assert L.up_peak_copy(FAKE, None, 16, None) == UP_ERR_INVALID
     assert L.up_peak_copy(FAKE, FAKE, 24, None) == UP_ERR_INVALID
     assert L.up_peak_copy(ctypes.c_void_p(0x1008), FAKE, 16, None) == UP_ERR_INVALID
+
+
+def test_linear_argument_validation(L):
+    def lin(x=FAKE, w=FAKE, y=FAKE, rows=100, n=512, k=256, act=0):
+        return L.up_linear_bf16(x, w, y, rows, None, n, k, act, None)
+
+    assert lin(x=None) == UP_ERR_INVALID
+    assert lin(y=None) == UP_ERR_INVALID
+    assert lin(rows=-1) == UP_ERR_INVALID
+    assert lin(n=300) == UP_ERR_UNSUPPORTED
+    assert lin(n=0) == UP_ERR_UNSUPPORTED
+    assert lin(k=100) == UP_ERR_UNSUPPORTED
+    assert lin(act=2) == UP_ERR_INVALID
+    assert lin(x=ctypes.c_void_p(0x1008)) == UP_ERR_INVALID  # not 16-byte aligned
+    assert lin(y=ctypes.c_void_p(0x1004)) == UP_ERR_INVALID  # not 8-byte aligned
+    assert lin(rows=1 << 20, k=4096) == UP_ERR_UNSUPPORTED  # x of 8 GiB: 32-bit offsets
+    assert "4 GiB" in L.up_last_error().decode()

@@ -455,3 +455,12 @@ def paged_given_cache(wl: Workload):
         kc[page, :, off, :] = K
         vc[page, :, off, :] = V
     return kc, vc
+
+
+def linear_inputs(seed: int, rows: int, k: int, n: int, x_scale: float = 1.0):
+    """Activations x [rows, k] ~ N(0, x_scale^2) and weights w [n, k] ~
+    N(0, 1/k) (so each output has about x_scale's spread), both bf16 bits."""
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits(_normal32(rng, (rows, k), x_scale))
+    w = f32_to_bf16_bits(_normal32(rng, (n, k), 1.0 / np.sqrt(k)))
+    return x, w
