@@ -241,15 +241,16 @@ def kernel_code_hash(path):
     return hashlib.sha256(" ".join(txt.split()).encode()).hexdigest()
 
 
-def traffic_from_profile(src_hash):
-    """HBM bytes per attention launch from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "attn_bf16_packed_llama8b_counters.md")
+def traffic_from_profile(src_hash, name="attn_bf16_packed_llama8b_counters.md"):
+    """HBM bytes per launch of a kernel from its committed counter summary
+    under profiles/, if the summary was taken on the current kernel source;
+    else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m = re.search(r"kernel code sha256[^:\n]*: ([0-9a-f]{64})", txt)
-    t = re.search(r"HBM bytes per launch \(scaled\): ([0-9.eE+]+)", txt)
+    t = re.search(r"HBM bytes per launch \(scaled\)[^:\n]*: ([0-9.eE+]+)", txt)
     if not m or not t or m.group(1) != src_hash:
         return None
     return float(t.group(1))
@@ -444,7 +445,11 @@ def run_propagation(args):
         "maps": res_maps,
         "roofline": {"bound": "mfma", "kernel": "linear_bf16_kernel", "map": dominant,
                      "achieved": dm["TFLOP/s_all"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dm["frac_all"], "traffic": None},
+                     "frac": dm["frac_all"],
+                     "traffic": traffic_from_profile(
+                         kernel_code_hash(os.path.join(ROOT, "block_sparse_token_amd", "csrc",
+                                                       "linear.hip")),
+                         "linear_bf16_later_layer_kernel_stats.md")},
     }
     if not args.no_cpu_baseline:
         # the oracle's four maps on the first kept rows, float64 on this host

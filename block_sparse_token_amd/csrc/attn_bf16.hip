@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lds_copy.h"
 
 namespace up {
 
@@ -47,7 +48,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) const char lchar;
 
 template <int D_>
 struct Cfg {
@@ -142,41 +142,6 @@ __device__ inline int first_key_at_or_after(const AttnArgs& a, const Seg& sg, in
 }
 
 // ----------------------------------------------------------------------------
-// direct global -> LDS copies and the waits around them
-// ----------------------------------------------------------------------------
-// The copies are issued from inline assembly, so the compiler neither counts
-// them nor guards LDS reads against them: every wait below is explicit.
-// Loads of one wave complete in issue order, so "at most N outstanding"
-// means every copy but the last N issued has landed.  LDS base in M0 (one
-// wait state before the copy reads it); lane i's bytes land at base + i*size.
-// The base is the same in every lane of the wave.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lchar*)p;
-}
-__device__ __forceinline__ void copy16(uintptr_t src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-__device__ __forceinline__ void copy4(uintptr_t src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory");
-}
-// this wave's outstanding global loads (copies included) <= N
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-// workgroup barrier that orders LDS only (no wait for outstanding copies)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-}
-
-// ----------------------------------------------------------------------------
 // tile staging
 // ----------------------------------------------------------------------------
 // Keys outside [0, u_end) are clamped to the nearest key in it (real,
@@ -209,8 +174,8 @@ struct Stager {
     const uintptr_t sm = (uintptr_t)(a.slot_mapping + sg.q0 + own);
     const uintptr_t ps = (uintptr_t)(a.positions + sg.q0 + min(own, sg.n - 1));
     const uint32_t dst = l0 + ring_off(k);
-    copy4(cached ? bt : sm, dst);
-    copy4(ps, dst + C::BN * 4);
+    lds_copy4(cached ? bt : sm, dst);
+    lds_copy4(ps, dst + C::BN * 4);
   }
 
   // tile k: K and V rows of this wave's keys into buffer k % NBUF, chunk
@@ -238,9 +203,9 @@ struct Stager {
       // 24-bit product: Hkv <= 255 (checked by the host), page * Hkv < 2^27
       // (a documented precondition on the cache size)
       const long rowb = (long)((__umul24(page, a.Hkv) + g) * kPageSize + off) * C::RBYTES;
-      copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,
+      lds_copy16((uintptr_t)a.k_cache + rowb + (pc ^ swk<C::D>(r)) * 16,
              dst + C::K_OFF + rbase * C::RBYTES);
-      copy16((uintptr_t)a.v_cache + rowb + (pc ^ swv<C::D>(r)) * 16,
+      lds_copy16((uintptr_t)a.v_cache + rowb + (pc ^ swv<C::D>(r)) * 16,
              dst + C::V_OFF + rbase * C::RBYTES);
     }
     // positions: a cached key's is its index, one outside the key range
@@ -262,15 +227,15 @@ struct Stager {
 // of the workgroup runs the same steps.
 template <class C>
 __device__ inline void sweep_prologue(const Stager<C>& st) {
-  lds_barrier();  // the previous users of the buffers and the ring are done
+  lds_only_barrier();  // the previous users of the buffers and the ring are done
 #pragma unroll
   for (int k = 0; k < C::IA; ++k) st.index(k);
-  wait_loads<0>();
-  lds_barrier();
+  lds_copy_wait<0>();
+  lds_only_barrier();
 #pragma unroll
   for (int k = 0; k < C::LA; ++k) st.data(k);
-  wait_loads<C::COPIES_DATA>();  // tile 0 has landed
-  lds_barrier();
+  lds_copy_wait<C::COPIES_DATA>();  // tile 0 has landed
+  lds_only_barrier();
 }
 // Only tiles that exist are copied: step t issues the index copies of tile
 // t+IA and the data copies of tile t+LA only while those are below nt, and
@@ -284,14 +249,14 @@ template <class C>
 __device__ inline void sweep_step_end(int t, int nt) {
   const bool w0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
   if (t + C::IA < nt) {
-    if (w0) wait_loads<C::COPIES_STEP>();
-    else wait_loads<C::COPIES_DATA>();
+    if (w0) lds_copy_wait<C::COPIES_STEP>();
+    else lds_copy_wait<C::COPIES_DATA>();
   } else if (t + C::LA < nt) {
-    wait_loads<C::COPIES_DATA>();
+    lds_copy_wait<C::COPIES_DATA>();
   } else {
-    wait_loads<0>();
+    lds_copy_wait<0>();
   }
-  lds_barrier();
+  lds_only_barrier();
 }
 
 // ----------------------------------------------------------------------------
@@ -521,11 +486,11 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   float* run_lse = row_scores ? a.score_part + (long)(i - r0s) * a.Hq + g * G + hh : nullptr;
   const long run_stride = (long)Bs * a.Hq;  // between consecutive runs
   const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(w),
-                     l, lds, lds_addr(lds)};
+                     l, lds, lds_addr_of(lds)};
 
   // S^T of tile t, masked where the tile is not entirely visible
   const FragOffsets<C> fo;
-  const uint32_t l0 = lds_addr(lds);
+  const uint32_t l0 = lds_addr_of(lds);
   auto qk = [&](int t) {
     const TileFrag<C> tf(fo, l0 + st.buf_off(t));
     const int* kpos = (const int*)(lds + st.ring_off(t) + C::BN * 4);
@@ -681,14 +646,14 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
     }
     // waves 4-7 finish the last tile (its buffer is no longer written)
     if (!lead && active) spv(nt - 1);
-    wait_loads<0>();
+    lds_copy_wait<0>();
   };
   int* misc = (int*)(lds + C::MISC_OFF);
   if (tid == 0) misc[1] = 0;  // published by the prologue's barriers
   if (item_scores) run(std::false_type{}, std::true_type{});
   else run(std::false_type{}, std::false_type{});
   if (__any(bad) && l == 0) misc[1] = 1;
-  lds_barrier();
+  lds_only_barrier();
   if (misc[1]) run(std::true_type{}, std::true_type{});
 
   // epilogue: normalise and store; lane holds d = db*32 + jg*8 + h*4 + e

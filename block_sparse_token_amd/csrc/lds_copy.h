@@ -25,6 +25,13 @@ __device__ __forceinline__ void lds_copy16(uintptr_t src, uint32_t lds_base) {
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
+// 4 bytes per lane from global address src to LDS at lds_base + lane * 4
+__device__ __forceinline__ void lds_copy4(uintptr_t src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
 // 16 bytes per lane from sbase + voff (sbase the same in every lane, voff a
 // 32-bit byte offset per lane) to LDS at lds_base + lane * 16
 __device__ __forceinline__ void lds_copy16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {

@@ -22,6 +22,14 @@ def test_counter_summary_is_read_when_its_hash_matches():
     assert bench.traffic_from_profile("0" * 64) is None
 
 
+def test_linear_counter_summary_is_read():
+    txt = open(os.path.join(ROOT, "profiles", "linear_bf16_later_layer_kernel_stats.md")).read()
+    hashes = re.findall(r"\b[0-9a-f]{64}\b", txt)
+    assert len(hashes) == 1
+    t = bench.traffic_from_profile(hashes[0], "linear_bf16_later_layer_kernel_stats.md")
+    assert t is not None and t > 0
+
+
 def test_kernel_hash_ignores_comments_and_whitespace(tmp_path):
     a = tmp_path / "a.hip"
     b = tmp_path / "b.hip"
