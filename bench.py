@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="throughput against the number of packed prompts, and packed vs "
+                         "bin-packed rows vs padded layouts of the headline batch")
     ap.add_argument("--propagation", action="store_true",
                     help="time one later layer's linear maps on all vs the kept tokens of the "
                          "headline batch")
@@ -472,6 +475,114 @@ def run_propagation(args):
     print(json.dumps(res), flush=True)
 
 
+def _time_one_call(torch, wl, steps, warmup):
+    """Stage a one-call workload on the GPU and time its whole step (rotary
+    and cache write, attention with block mass, scores, top-p, compaction);
+    returns (ms per step, attention kernel ms, visible pairs, kept tokens)."""
+    from workloads import device as WD
+    from block_sparse_token_amd import binding as B
+    from block_sparse_token_amd import step as ST
+
+    call = wl.calls[0]
+    kc, vc = WD.make_caches(wl)
+    batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
+                          call.block_table)
+    pc = ST.PrefillCall(batch=batch, q=WD.stored_to_tensor(call.q), k=WD.stored_to_tensor(call.k),
+                        v=WD.stored_to_tensor(call.v), k_cache=kc, v_cache=vc,
+                        num_blocks=call.num_blocks(wl.block_size),
+                        flags=torch.from_numpy(call.flags.astype(np.uint8)).cuda(),
+                        block_size=wl.block_size, p=wl.p, rope_theta=wl.theta,
+                        rows=WD.row_sources(call))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pc.launch()
+    torch.cuda.synchronize()
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)  # creates the underlying event the library records
+        return e
+
+    evs = [(ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        B.up_profile_attn_events(a, b)
+        pc.launch()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    B.up_profile_attn_events()
+    attn = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pairs = visible_pairs(call.cu_seqlens, call.ctx_lens, call.positions, 0)
+    kept = int(pc.num_kept.item())
+    del pc, kc, vc
+    torch.cuda.empty_cache()
+    return wall, attn, pairs, kept
+
+
+def run_sweep(args):
+    """Operator throughput against the number of packed prompts, and the
+    padding comparison of the Prepacking summary ("Key design"): the
+    headline batch's 16 prompts run (a) packed back to back, the operator's
+    own layout, (b) bin-packed by first-fit decreasing into rows of the
+    longest prompt's length, each row padded at its end, (c) each prompt
+    padded to the longest.  Padding tokens are ordinary tokens to the
+    operator (they cost what real ones cost) and are not scored.  Prints one
+    JSON line."""
+    import torch
+    import workloads as W
+    from block_sparse_token_amd import packing as PK
+
+    common = dict(Hq=32, Hkv=8, D=128, dtype="bf16", block_size=64, p=0.95, theta=500000.0,
+                  hidden_width=4096, scale=1.0 / np.sqrt(128.0))
+
+    def entry(S, T, useful, ms, attn, pairs, kept):
+        fl = 4.0 * 128 * 32 * pairs
+        return {"prompts": S, "tokens": T, "useful_tokens": useful, "kept_tokens": kept,
+                "ms_per_step": ms, "useful_tokens_per_s": useful / (ms * 1e-3),
+                "attention_ms": attn, "attention_frac_of_bf16_peak":
+                    fl / (attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+    sweep = []
+    for S in (1, 2, 4, 8, 16, 32):
+        lengths = [int(x) for x in np.random.default_rng(100 + S).integers(512, 8193, size=S)]
+        wl = W.custom(lengths=lengths, seed=100 + S, **common)
+        ms, attn, pairs, kept = _time_one_call(torch, wl, args.steps, args.warmup)
+        T = int(sum(lengths))
+        sweep.append(entry(S, T, T, ms, attn, pairs, kept))
+        print(f"sweep prompts={S} tokens={T} ms={ms:.3f}", file=sys.stderr, flush=True)
+
+    head = W.make(WORKLOAD)
+    lengths = [s.n for s in head.calls[0].segments]
+    T = int(sum(lengths))
+    cap = max(lengths)
+    layouts = {}
+    ms, attn, pairs, kept = _time_one_call(torch, head, args.steps, args.warmup)
+    layouts["packed"] = dict(entry(len(lengths), T, T, ms, attn, pairs, kept), pad_tokens=0)
+    del head
+    segs, pad_flags, pad, nrows = PK.bin_packed_segments(lengths, cap)
+    wl = W.custom(lengths=segs, flags=[not f for f in pad_flags], seed=7, **common)
+    ms, attn, pairs, kept = _time_one_call(torch, wl, args.steps, args.warmup)
+    layouts["bin_packed_rows"] = dict(entry(len(lengths), sum(segs), T, ms, attn, pairs, kept),
+                                      pad_tokens=pad, rows=nrows, row_capacity=cap)
+    print(f"bin-packed rows={nrows} pad={pad} ms={ms:.3f}", file=sys.stderr, flush=True)
+    del wl
+    segs, pad = PK.padded_lengths(lengths)
+    wl = W.custom(lengths=segs, seed=8, **common)
+    ms, attn, pairs, kept = _time_one_call(torch, wl, args.steps, args.warmup)
+    layouts["padded"] = dict(entry(len(lengths), sum(segs), T, ms, attn, pairs, kept),
+                             pad_tokens=pad)
+    print(f"padded pad={pad} ms={ms:.3f}", file=sys.stderr, flush=True)
+    res = {"metric": "packed prefill tokens/s vs packed prompts; packed vs bin-packed rows vs "
+                     "padded (useful tokens/s)",
+           "unit": "tokens/s", "higher_is_better": True, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "prompts with lengths uniform in [512, 8192] (seed 100 + "
+                                  "prompts), 32/8 heads x 128, rope 5e5, block 64, top-p 0.95, "
+                                  "hidden 4096; padding comparison on the headline batch"},
+           "sweep": sweep, "padding": layouts}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -492,6 +603,9 @@ def main():
 
     if args.propagation:
         run_propagation(args)
+        return
+    if args.sweep:
+        run_sweep(args)
         return
     if args.workload != WORKLOAD:
         run_other_workload(args)

@@ -105,3 +105,16 @@ def test_gpu_most_segments_per_call():
     wl = W.custom(seed=4096, hidden_width=16, lengths=lengths, ctxs=ctxs, flags=flags, Hq=4,
                   Hkv=2, D=64, dtype="bf16", block_size=16, p=0.9, theta=500000.0)
     assert _run_and_check(wl)
+
+
+def test_gpu_bin_packed_rows_with_padding_segments():
+    """Prompts bin-packed into rows of a fixed capacity, each row closed by an
+    unscored padding segment (the layout bench.py --sweep times against the
+    packed one)."""
+    from block_sparse_token_amd import packing as PK
+    segs, pad_flags, pad, nrows = PK.bin_packed_segments([100, 37, 250, 64, 180, 256, 5], 256)
+    assert pad > 0 and nrows >= 4
+    wl = W.custom(seed=4242, hidden_width=64, lengths=segs, flags=[not f for f in pad_flags],
+                  Hq=8, Hkv=2, D=128, dtype="bf16", block_size=64, p=0.95, theta=500000.0,
+                  scale=1.0 / np.sqrt(128.0))
+    assert _run_and_check(wl)
