@@ -357,13 +357,15 @@ def cpu_baseline(wl, call, budget_s):
 
 def run_propagation(args):
     """Payoff of the selection in the later layers: one Llama-3.1-8B-shaped
-    later layer's linear maps (query/key/value projection 4096 -> 6144,
-    output projection 4096 -> 4096, SwiGLU gate and up projections 4096 ->
-    2 x 14336, down projection 14336 -> 4096; random bf16 weights) run on all
-    tokens of the headline batch and on the tokens its selection kept (the
-    compacted hidden states, with the kept count read on the device).  The
-    output projection takes the hidden states as its input (the attention
-    output of a later layer has the same shape).  Prints one JSON line."""
+    later layer of a linear/full hybrid - query/key/value projection 4096 ->
+    6144, causal linear attention (phi = elu + 1) over each prompt's rows,
+    output projection 4096 -> 4096 of its result, SwiGLU gate and up
+    projections 4096 -> 2 x 14336 and down projection 14336 -> 4096; random
+    bf16 weights - runs on all tokens of the headline batch and on the tokens
+    its selection kept (the compacted hidden states and per-prompt kept
+    counts, with the kept total read on the device).  The MLP takes the
+    hidden states as its input (no norms or residuals: their cost does not
+    change the comparison).  Prints one JSON line."""
     import torch
     import oracle
     from block_sparse_token_amd import binding as B
@@ -389,56 +391,74 @@ def run_propagation(args):
     x_all = dict(pc.rows)["hidden"]
     x_kept = pc.rows_out["hidden"]
     qkv = torch.empty((T, QKV), dtype=torch.bfloat16, device="cuda")
+    attn = torch.zeros((T, wl.Hq, D), dtype=torch.bfloat16, device="cuda")
+    q_v = qkv[:, : wl.Hq * D].view(T, wl.Hq, D)
+    k_v = qkv[:, wl.Hq * D: (wl.Hq + wl.Hkv) * D].view(T, wl.Hkv, D)
+    v_v = qkv[:, (wl.Hq + wl.Hkv) * D:].view(T, wl.Hkv, D)
     o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     hmid = torch.empty((T, MLP), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-    maps = [("qkv", H, QKV), ("o", H, H), ("gate_up_swiglu", H, 2 * MLP), ("down", MLP, H)]
+    maps = [("qkv", H, QKV), ("linear_attention", None, None), ("o", H, H),
+            ("gate_up_swiglu", H, 2 * MLP), ("down", MLP, H)]
     stream = torch.cuda.current_stream()
+    cu_all = pc.batch.cu_seqlens
 
-    def layer(x, rows_dev, ev=None):
-        args_ = [(x, w_qkv, qkv, B.UP_ACT_NONE), (x, w_o, o, B.UP_ACT_NONE),
+    def layer(x, rows_dev, cu, ev=None):
+        args_ = [(x, w_qkv, qkv, B.UP_ACT_NONE), None, (attn.view(T, H), w_o, o, B.UP_ACT_NONE),
                  (x, w_gu, hmid, B.UP_ACT_SWIGLU), (hmid, w_down, y, B.UP_ACT_NONE)]
-        for j, (inp, w, out, act) in enumerate(args_):
+        for j, a_ in enumerate(args_):
             if ev is not None:
                 ev[j][0].record(stream)
-            B.up_linear_bf16(inp, w, out, rows_in_use=rows_dev, act=act)
+            if a_ is None:
+                B.up_linear_attn_bf16(cu, q_v, k_v, v_v, attn)
+            else:
+                inp, w, out, act = a_
+                B.up_linear_bf16(inp, w, out, rows_in_use=rows_dev, act=act)
             if ev is not None:
                 ev[j][1].record(stream)
 
-    def timed(x, rows_dev):
+    def timed(x, rows_dev, cu):
         for _ in range(args.warmup):
-            layer(x, rows_dev)
+            layer(x, rows_dev, cu)
         torch.cuda.synchronize()
         evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in maps] for _ in range(args.steps)]
         t0 = time.perf_counter()
         for ev in evs:
-            layer(x, rows_dev, ev)
+            layer(x, rows_dev, cu, ev)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / args.steps
         per_map = [float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for ev in evs]))
                    for j in range(len(maps))]
         return wall, per_map
 
-    wall_all, ms_all = timed(x_all, None)
-    wall_kept, ms_kept = timed(x_kept, pc.num_kept)
+    wall_all, ms_all = timed(x_all, None, cu_all)
+    wall_kept, ms_kept = timed(x_kept, pc.num_kept, pc.cu_seqlens_out)
     res_maps = {}
+    # linear attention, recurrent-form flops per token: the state update per
+    # KV head, numerator and denominator per query head
+    la_per_tok = 2.0 * wl.Hkv * D * D + wl.Hq * (2.0 * D * D + 2.0 * D)
     for j, (name, K, N) in enumerate(maps):
-        f_all, f_kept = 2.0 * T * K * N, 2.0 * kept * K * N
-        res_maps[name] = {"K": K, "N": N, "ms_all": ms_all[j], "ms_kept": ms_kept[j],
+        if K is None:
+            f_all, f_kept = la_per_tok * T, la_per_tok * kept
+        else:
+            f_all, f_kept = 2.0 * T * K * N, 2.0 * kept * K * N
+        res_maps[name] = {"K": K, "N": N, "flops_all": f_all, "ms_all": ms_all[j],
+                          "ms_kept": ms_kept[j],
                           "TFLOP/s_all": f_all / (ms_all[j] * 1e-3) / 1e12,
                           "TFLOP/s_kept": f_kept / (ms_kept[j] * 1e-3) / 1e12,
                           "frac_all": f_all / (ms_all[j] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    flops_all = oracle.later_layer_flops(T, H, QKV, MLP)
-    flops_kept = oracle.later_layer_flops(kept, H, QKV, MLP)
+    flops_all = oracle.later_layer_flops(T, H, QKV, MLP) + la_per_tok * T
+    flops_kept = oracle.later_layer_flops(kept, H, QKV, MLP) + la_per_tok * kept
     dominant = max(res_maps, key=lambda k: res_maps[k]["ms_all"])
     dm = res_maps[dominant]
     res = {
-        "metric": "later-layer linear maps on the kept tokens vs all tokens (ms per layer)",
+        "metric": "later layer on the kept tokens vs all tokens (ms per layer)",
         "value": wall_kept, "unit": "ms", "higher_is_better": False, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "one Llama-3.1-8B-shaped later layer (4096 -> 6144, 4096 -> 4096, "
-                               "SwiGLU 4096 -> 2 x 14336, 14336 -> 4096) on the packed prefill of "
+        "config": {"workload": "one Llama-3.1-8B-shaped later linear-attention layer (4096 -> 6144, "
+                               "causal linear attention 32/8 heads x 128, 4096 -> 4096, SwiGLU "
+                               "4096 -> 2 x 14336, 14336 -> 4096) on the packed prefill of "
                                f"{T} tokens, {kept} kept by top-p 0.95 (block 64)",
                    "rows_all": T, "rows_kept": kept},
         "layer_ms_all": wall_all, "layer_ms_kept": wall_kept,
@@ -461,16 +481,22 @@ def run_propagation(args):
         ws = {k: v.float().cpu().numpy().astype(np.float64)
               for k, v in (("qkv", w_qkv), ("o", w_o), ("gate", w_gate), ("up", w_up),
                            ("down", w_down))}
+        cu_k = [int(c) for c in pc.cu_seqlens_out.cpu().numpy() if c < n] + [n]
+        Hq, Hkv = wl.Hq, wl.Hkv
         t0 = time.perf_counter()
-        oracle.linear(xs, ws["qkv"])
-        oracle.linear(xs, ws["o"])
+        qkv_s = oracle.linear(xs, ws["qkv"])
+        att = oracle.linear_attention(qkv_s[:, : Hq * D].reshape(n, Hq, D),
+                                      qkv_s[:, Hq * D: (Hq + Hkv) * D].reshape(n, Hkv, D),
+                                      qkv_s[:, (Hq + Hkv) * D:].reshape(n, Hkv, D), cu_k)
+        oracle.linear(att.reshape(n, Hq * D), ws["o"])
         hs = oracle.swiglu(xs, ws["gate"], ws["up"])
         oracle.linear(hs, ws["down"])
         spent = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": n / spent, "unit": "rows/s", "cores": default_threads(),
                                "kind": "oracle",
-                               "sample": f"{n} kept rows through the four maps, float64 NumPy "
-                                         f"matrix products, {spent:.2f} s",
+                               "sample": f"the first {n} kept rows through the layer (linear "
+                                         f"maps, linear attention over their prompts), float64 "
+                                         f"NumPy, {spent:.2f} s",
                                "gpu_rows_per_s_kept": kept / (wall_kept * 1e-3)}
     print(json.dumps(res), flush=True)
 

@@ -70,6 +70,9 @@ def lib():
             "up_check_batch": (c_i32, [bp, c_i32, c_vp, c_vp]),
             "up_peak_mfma_bf16": (c_i32, [c_i32, c_i32, c_vp, c_vp]),
             "up_peak_copy": (c_i32, [c_vp, c_vp, c_size, c_vp]),
+            "up_linear_attn_bf16": (c_i32, [c_vp, c_i32, c_vp, ctypes.c_int64, c_vp,
+                                            ctypes.c_int64, c_vp, ctypes.c_int64, c_i32, c_i32,
+                                            c_i32, c_vp, c_vp]),
             "up_linear_bf16": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
@@ -85,7 +88,7 @@ def lib():
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
-            "up_peak_copy", "up_linear_bf16"]
+            "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16"]
 
 
 def _check(st: int, what: str):
@@ -259,3 +262,26 @@ def interleave_gate_up(w_gate, w_up):
         raise UniprefillError("gate and up weights must share a shape [F, K], F a multiple of 128")
     return torch.stack([w_gate.reshape(F // 32, 32, K), w_up.reshape(F // 32, 32, K)],
                        dim=1).reshape(2 * F, K).contiguous()
+
+
+def up_linear_attn_bf16(cu_seqlens, q, k, v, out, stream=None):
+    """Causal linear attention (phi = elu + 1) over each segment of
+    ``cu_seqlens``.  q [rows, Hq, D] and k, v [rows, Hkv, D] bfloat16 views
+    whose rows may be strided (e.g. column ranges of one projection output,
+    ``qkv[:, :Hq*D].view(rows, Hq, D)``); out [rows, Hq, D] contiguous."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.device.type != "cuda":
+            raise UniprefillError(f"{name} must be a 3-D bfloat16 GPU tensor")
+        if t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise UniprefillError(f"{name}: heads must be contiguous within a row")
+    if not out.is_contiguous():
+        raise UniprefillError("out must be contiguous")
+    rows, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != rows or out.shape != q.shape:
+        raise UniprefillError("q, k, v and out shapes do not match")
+    _check(lib().up_linear_attn_bf16(_p(cu_seqlens), cu_seqlens.numel() - 1,
+                                     ctypes.c_void_p(q.data_ptr()), q.stride(0),
+                                     ctypes.c_void_p(k.data_ptr()), k.stride(0),
+                                     ctypes.c_void_p(v.data_ptr()), v.stride(0), Hq, Hkv, D,
+                                     _p(out), _stream(stream)), "up_linear_attn_bf16")

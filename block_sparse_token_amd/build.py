@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libuniprefill.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "plan.hip", "rope_kv.hip", "attn_bf16.hip", "attn_f32.hip", "select.hip",
-           "compact.hip", "peaks.hip", "mass.hip", "linear.hip"]
+           "compact.hip", "peaks.hip", "mass.hip", "linear.hip",
+           "linear_attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -133,6 +133,28 @@ up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return device_status(up::launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak copy launch");
 }
 
+up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
+                              int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                              int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              void* out, void* stream) {
+  if (!cu_seqlens || !q || !k || !v || !out)
+    return fail(UP_ERR_INVALID, "cu_seqlens, q, k, v and out must be non-NULL");
+  if (num_seqs <= 0) return fail(UP_ERR_INVALID, "num_seqs must be >= 1 (got %d)", num_seqs);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv || Hq > 65535)
+    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d), at most 65535", Hq,
+                Hkv);
+  if (head_dim != 128) return fail(UP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (q_stride < (int64_t)Hq * head_dim || k_stride < (int64_t)Hkv * head_dim ||
+      v_stride < (int64_t)Hkv * head_dim || (q_stride | k_stride | v_stride) % 8)
+    return fail(UP_ERR_INVALID, "row strides must hold all heads and be multiples of 8 elements");
+  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) & 15)
+    return fail(UP_ERR_INVALID, "q, k and v must be 16-byte aligned");
+  if (((uintptr_t)out) & 1) return fail(UP_ERR_INVALID, "out must be 2-byte aligned");
+  return device_status(up::launch_linear_attn_bf16(cu_seqlens, num_seqs, q, q_stride, k, k_stride,
+                                                   v, v_stride, Hq, Hkv, out, as_stream(stream)),
+                       "linear attention launch");
+}
+
 up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap,
                          const int32_t* rows_in_use, int32_t n_out, int32_t k_in, int32_t act,
                          void* stream) {

@@ -1,0 +1,265 @@
+// Causal linear attention over the kept tokens of each packed segment, on
+// bf16 matrix cores (gfx950): a later linear-attention layer of a
+// linear/full hybrid running on the compacted rows only.
+//
+// What is computed (UniPrefill paper entry, abstract: linear/full hybrid
+// models; review, "Method & Key Results": dropped tokens skip every later
+// sublayer): per segment and query head h (KV head g = h / G), with
+// phi(x) = elu(x) + 1 (Katharopoulos et al., "Transformers are RNNs",
+// 2020), o_t = phi(q_t)^T S_t / (phi(q_t) . z_t), S_t = sum over s <= t of
+// phi(k_s) v_s^T, z_t = sum of phi(k_s), s ranging over the segment's own
+// tokens in order.
+//
+// Chunked form: the segment is walked in chunks of 64 tokens by one
+// workgroup per (segment, query head), four waves.  For chunk c with
+// states S, z of the chunks before it:
+//   A   = mask(phi(Q_c) phi(K_c)^T)           (64 x 64, key <= query)
+//   o_c = (A V_c + phi(Q_c) S) / (A 1 + phi(Q_c) z)
+//   S  += phi(K_c)^T V_c,   z += phi(K_c)^T 1
+// All four products run on v_mfma_f32_32x32x16_bf16.  S stays in float32
+// registers (wave w owns output columns 32w..32w+31); for the product
+// phi(Q_c) S it is handed over in LDS as the bf16 pair hi + lo (hi the
+// rounding of S, lo that of the remainder), so S enters with about 16
+// significant bits.  The denominators use the same bf16 A and phi(K) as the
+// numerators.  LDS tiles are row-major with 16-byte chunks XOR-swizzled per
+// row, so fragment reads of 16 rows fall on distinct banks; phi(K) and V
+// are also stored transposed (key-minor), which is the layout the products
+// over keys read.
+#include "common.h"
+#include "lds_copy.h"
+
+namespace up {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
+
+constexpr int kC = 64;   // tokens per chunk
+constexpr int kD = 128;  // head dimension
+constexpr int kThreads = 256;
+// LDS layout (bytes)
+constexpr int QF = 0;                  // phi(Q) [64][128]   rows of 256 B
+constexpr int KF = QF + kC * kD * 2;   // phi(K) [64][128]
+constexpr int KT = KF + kC * kD * 2;   // phi(K)^T [128][64] rows of 128 B
+constexpr int VT = KT + kD * kC * 2;   // V^T [128][64]
+constexpr int AB = VT + kD * kC * 2;   // A [64][64]         rows of 128 B
+constexpr int SH = AB + kC * kC * 2;   // S^T hi [128][128]   rows of 256 B
+constexpr int SL = SH + kD * kD * 2;   // S^T lo
+constexpr int ZF = SL + kD * kD * 2;   // z [128] f32
+constexpr int DN = ZF + kD * 4;        // denominators [64] f32
+constexpr int kLdsBytes = DN + kC * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
+
+// byte offset of element (r, e) in a row-major bf16 tile with 256-byte rows
+__device__ inline int off256(int r, int e) { return r * 256 + ((((e >> 3) ^ (r & 15))) << 4) + (e & 7) * 2; }
+// ... with 128-byte rows
+__device__ inline int off128(int r, int e) { return r * 128 + ((((e >> 3) ^ ((r >> 1) & 7))) << 4) + (e & 7) * 2; }
+
+__device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+struct LinAttnArgs {
+  const int32_t* cu_seqlens;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  long q_stride, k_stride, v_stride;  // elements between consecutive tokens
+  int Hq, Hkv;
+  uint16_t* out;  // [rows, Hq, 128]
+};
+
+__device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int g = h / (a.Hq / a.Hkv);
+  const int t_begin = a.cu_seqlens[s], t_end = a.cu_seqlens[s + 1];
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t L0 = lds_addr_of(lds);
+
+  // S^T hi/lo and z start at zero
+  for (int i = tid; i < (2 * kD * kD * 2 + kD * 4) / 16; i += kThreads)
+    *(u32x4*)(lds + SH + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  f32x16 sacc[4];  // S[32i + row][32w + col] blocks, i = d_in block
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[i][e] = 0.f;
+  __syncthreads();
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kC) {
+    const int nrows = min(kC, t_end - t0);
+    // (a) the chunk's phi(q), phi(k), v into LDS; rows past the segment are
+    // zero (not phi(0)), so they add nothing to A, S or z
+#pragma unroll
+    for (int p = tid; p < kC * 16; p += kThreads) {
+      const int r = p >> 4, c = p & 15;
+      const bool ok = r < nrows;
+      u32x4 qr = {0u, 0u, 0u, 0u}, kr = qr, vr = qr;
+      if (ok) {
+        const long t = t0 + r;
+        qr = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
+        kr = *(const u32x4*)(a.k + t * a.k_stride + (long)g * kD + c * 8);
+        vr = *(const u32x4*)(a.v + t * a.v_stride + (long)g * kD + c * 8);
+      }
+      bf16x8 fq, fk;
+      const uint16_t* q16 = (const uint16_t*)&qr;
+      const uint16_t* k16 = (const uint16_t*)&kr;
+      const uint16_t* v16 = (const uint16_t*)&vr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        fq[e] = ok ? (__bf16)phi(bf2f(q16[e])) : (__bf16)0.f;
+        fk[e] = ok ? (__bf16)phi(bf2f(k16[e])) : (__bf16)0.f;
+      }
+      *(bf16x8*)(lds + QF + off256(r, c * 8)) = fq;
+      *(bf16x8*)(lds + KF + off256(r, c * 8)) = fk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        *(__bf16*)(lds + KT + off128(c * 8 + e, r)) = fk[e];
+        *(uint16_t*)(lds + VT + off128(c * 8 + e, r)) = v16[e];
+      }
+    }
+    __syncthreads();
+
+    // (b) wave w: A block (rows 32 (w >> 1).., keys 32 (w & 1)..), masked,
+    // to LDS in bf16; and this chunk's phi(K)^T V into S (registers)
+    {
+      const int mr = w >> 1, nc = w & 1;
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mr * 32 + l32, ks * 16 + hl * 8));
+        const bf16x8 kb = *(lbf16x8*)(uintptr_t)(L0 + KF + off256(nc * 32 + l32, ks * 16 + hl * 8));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, acc, 0, 0, 0);
+      }
+      const int key = nc * 32 + l32;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = mr * 32 + jj * 8 + hl * 4 + e;
+          *(__bf16*)(lds + AB + off128(row, key)) = (__bf16)(key <= row ? acc[jj * 4 + e] : 0.f);
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 ka = *(lbf16x8*)(uintptr_t)(L0 + KT + off128(i * 32 + l32, ks * 16 + hl * 8));
+          sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, sacc[i], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+
+    // (c) denominators: row r = tid / 4, quarter x = tid % 4 sums A[r][16x..]
+    // and phi(Q)[r][32x..] . z (z of the chunks before this one)
+    {
+      const int r = tid >> 2, x = tid & 3;
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) d += (float)*(const __bf16*)(lds + AB + off128(r, x * 16 + e));
+      const float* z = (const float*)(lds + ZF);
+#pragma unroll 8
+      for (int e = 0; e < 32; ++e) d += (float)*(const __bf16*)(lds + QF + off256(r, x * 32 + e)) * z[x * 32 + e];
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      if (x == 0) ((float*)(lds + DN))[r] = d;
+    }
+    __syncthreads();
+
+    // (d) wave w: outputs of columns 32w.. for both 32-row blocks:
+    // A V + phi(Q) (S_hi + S_lo), divided by the row's denominator
+    {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 aa = *(lbf16x8*)(uintptr_t)(L0 + AB + off128(mb * 32 + l32, ks * 16 + hl * 8));
+          const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mb * 32 + l32, ks * 16 + hl * 8));
+          const bf16x8 sh = *(lbf16x8*)(uintptr_t)(L0 + SH + off256(w * 32 + l32, ks * 16 + hl * 8));
+          const bf16x8 sl = *(lbf16x8*)(uintptr_t)(L0 + SL + off256(w * 32 + l32, ks * 16 + hl * 8));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc, 0, 0, 0);
+        }
+        const float* den = (const float*)(lds + DN);
+        const int col = w * 32 + l32;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = mb * 32 + jj * 8 + hl * 4 + e;
+            if (row < nrows) {
+              const float o = acc[jj * 4 + e] / den[row];
+              *(__bf16*)(a.out + ((long)(t0 + row) * a.Hq + h) * kD + col) = (__bf16)o;
+            }
+          }
+      }
+    }
+    __syncthreads();
+
+    // (e) hand S over for the next chunk (hi + lo, transposed), and add this
+    // chunk's keys to z
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = sacc[i][jj * 4 + e];
+          hi[e] = (__bf16)x;
+          lo[e] = (__bf16)(x - (float)hi[e]);
+        }
+        const int dout = w * 32 + l32, din = i * 32 + jj * 8 + hl * 4;
+        *(bf16x4*)(lds + SH + off256(dout, din)) = hi;
+        *(bf16x4*)(lds + SL + off256(dout, din)) = lo;
+      }
+    if (tid < kD) {
+      float zs = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < kC; ++e) zs += (float)*(const __bf16*)(lds + KT + off128(tid, e));
+      ((float*)(lds + ZF))[tid] += zs;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void* q, long q_stride,
+                                   const void* k, long k_stride, const void* v, long v_stride,
+                                   int Hq, int Hkv, void* out, hipStream_t st) {
+  LinAttnArgs a;
+  a.cu_seqlens = cu_seqlens;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.q_stride = q_stride;
+  a.k_stride = k_stride;
+  a.v_stride = v_stride;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.out = (uint16_t*)out;
+  hipError_t e = hipFuncSetAttribute((const void*)linear_attn_bf16_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(linear_attn_bf16_kernel, dim3(S, Hq), dim3(kThreads), kLdsBytes, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace up

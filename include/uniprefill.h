@@ -236,6 +236,28 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
  * the rows used are not written.  n_out: a multiple of 256; k_in: a
  * multiple of 64; x and w each under 4 GiB (UP_ERR_UNSUPPORTED otherwise).
  */
+/*
+ * Later causal linear-attention layer on the kept tokens (UniPrefill paper
+ * entry, abstract: linear/full hybrid models; review, Method & Key Results:
+ * dropped tokens skip every later sublayer).  For every segment s (rows
+ * [cu_seqlens[s], cu_seqlens[s+1]), e.g. the cu_seqlens_out of up_compact)
+ * and query head h with KV head g = h / (Hq / Hkv), phi(x) = elu(x) + 1
+ * (Katharopoulos et al. 2020):
+ *   out[t][h] = phi(q_t,h)^T S_t / (phi(q_t,h) . z_t),
+ *   S_t = sum over the segment's rows r <= t of phi(k_r,g) v_r,g^T,
+ *   z_t = sum of phi(k_r,g).
+ * q, k, v: bf16 rows (token r's head j at base + r * stride + j * head_dim;
+ * strides in elements, multiples of 8, so the q, k and v column ranges of
+ * one [rows, (Hq + 2 Hkv) * head_dim] projection output can be passed
+ * directly), 16-byte aligned.  out: [rows, Hq, head_dim] bf16; rows outside
+ * the segments are not written.  head_dim must be 128 (UP_ERR_UNSUPPORTED).
+ * Device precondition: cu_seqlens non-decreasing.
+ */
+up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
+                              int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                              int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              void* out, void* stream);
+
 #define UP_ACT_NONE 0
 #define UP_ACT_SWIGLU 1
 up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap,

@@ -15,4 +15,4 @@ from .prefill import (  # noqa: F401
     topp_select,
     visible,
 )
-from .layers import later_layer_flops, linear, silu, swiglu  # noqa: F401
+from .layers import feature_map, later_layer_flops, linear, linear_attention, silu, swiglu  # noqa: F401

@@ -50,3 +50,42 @@ def later_layer_flops(rows: int, hidden: int = 4096, qkv_out: int = 6144,
     and up projections and the down projection."""
     per_row = hidden * qkv_out + hidden * hidden + 2 * hidden * mlp + mlp * hidden
     return 2 * rows * per_row
+
+
+def feature_map(x: np.ndarray) -> np.ndarray:
+    """phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise (always > 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqlens) -> np.ndarray:
+    """Causal linear attention over each segment of a packed batch, in the
+    recurrent form of Katharopoulos et al. ("Transformers are RNNs", 2020):
+    per head, with g the KV head of query head h,
+        S_t = S_{t-1} + phi(k_t) v_t^T,   z_t = z_{t-1} + phi(k_t),
+        o_t = phi(q_t)^T S_t / (phi(q_t) . z_t),
+    S and z starting at zero at every segment start (segments are the kept
+    tokens of one prompt in their original order; the hybrid models the
+    pages name interleave such layers with full attention, UniPrefill paper
+    entry, abstract).  q [T, Hq, D], k and v [T, Hkv, D]; returns float64
+    [T, Hq, D]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D), np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    for s in range(len(cu) - 1):
+        S = np.zeros((Hkv, D, D))
+        z = np.zeros((Hkv, D))
+        for t in range(cu[s], cu[s + 1]):
+            fk = feature_map(k[t])                       # [Hkv, D]
+            S += fk[:, :, None] * v[t][:, None, :]
+            z += fk
+            fq = feature_map(q[t]).reshape(Hkv, G, D)    # query heads of each group
+            num = np.einsum("gjd,gde->gje", fq, S)
+            den = np.einsum("gjd,gd->gj", fq, z)
+            out[t] = (num / den[:, :, None]).reshape(Hq, D)
+    return out

@@ -176,3 +176,19 @@ def test_linear_argument_validation(L):
     assert lin(y=ctypes.c_void_p(0x1004)) == UP_ERR_INVALID  # not 8-byte aligned
     assert lin(rows=1 << 20, k=4096) == UP_ERR_UNSUPPORTED  # x of 8 GiB: 32-bit offsets
     assert "4 GiB" in L.up_last_error().decode()
+
+
+def test_linear_attention_argument_validation(L):
+    def la(cu=FAKE, S=2, q=FAKE, qs=4096, k=FAKE, ks=1024, v=FAKE, vs=1024, Hq=32, Hkv=8, D=128,
+           out=FAKE):
+        return L.up_linear_attn_bf16(cu, S, q, qs, k, ks, v, vs, Hq, Hkv, D, out, None)
+
+    assert la(cu=None) == UP_ERR_INVALID
+    assert la(out=None) == UP_ERR_INVALID
+    assert la(S=0) == UP_ERR_INVALID
+    assert la(Hq=30) == UP_ERR_INVALID
+    assert la(D=64) == UP_ERR_UNSUPPORTED
+    assert la(qs=4000) == UP_ERR_INVALID  # cannot hold 32 heads of 128
+    assert la(ks=1028) == UP_ERR_INVALID  # not a multiple of 8
+    assert la(q=ctypes.c_void_p(0x1008)) == UP_ERR_INVALID
+    assert la(out=ctypes.c_void_p(0x1001)) == UP_ERR_INVALID

@@ -1,0 +1,70 @@
+"""Parity of the later linear-attention layer on the GPU
+(up_linear_attn_bf16) with the float64 oracle (oracle.linear_attention, the
+recurrent form).
+
+Tolerance: the bf16 output bound, |gpu - oracle| <= 2e-2 per element.  The
+GPU takes phi(q), phi(k) and the chunk's weights in bf16 (relative error
+2^-9 each) and the running state as a bf16 pair (about 2^-17); with v ~
+N(0, 1) the outputs are weighted means of values, so these relative
+errors of the weights move an output by a small fraction of the values'
+spread.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from block_sparse_token_amd import binding as Bd
+from block_sparse_token_amd import step as ST
+
+from gpu_harness import log
+
+pytestmark = pytest.mark.gpu
+
+ABS = 2e-2
+SENTINEL = -12288.0
+
+
+def _f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _run(lengths, Hq, Hkv, seed, lead=0, tail=0, strided=False):
+    D = 128
+    cu = np.concatenate([[lead], lead + np.cumsum(lengths)]).astype(np.int32)
+    rows = int(cu[-1]) + tail
+    log(f"linear attention lengths={lengths} Hq={Hq} Hkv={Hkv} lead={lead} tail={tail} "
+        f"strided={strided}")
+    qb, kb, vb = W.attention_inputs(seed, rows, Hq, Hkv, D)
+    q, k, v = (ST.stored_to_tensor(x) for x in (qb, kb, vb))
+    if strided:  # q, k, v as column ranges of one projection output
+        qkv = torch.cat([q.reshape(rows, -1), k.reshape(rows, -1), v.reshape(rows, -1)], dim=1)
+        q = qkv[:, : Hq * D].view(rows, Hq, D)
+        k = qkv[:, Hq * D: (Hq + Hkv) * D].view(rows, Hkv, D)
+        v = qkv[:, (Hq + Hkv) * D:].view(rows, Hkv, D)
+    out = torch.full((rows, Hq, D), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    cu_t = torch.from_numpy(cu).cuda()
+    Bd.up_linear_attn_bf16(cu_t, q, k, v, out)
+    torch.cuda.synchronize()
+    got = _f64(out)
+    a, b = int(cu[0]), int(cu[-1])
+    ref = oracle.linear_attention(W.to_f64(qb[a:b], "bf16"), W.to_f64(kb[a:b], "bf16"),
+                                  W.to_f64(vb[a:b], "bf16"), cu - a)
+    err = np.abs(got[a:b] - ref)
+    log(f"  max abs err {err.max():.3e}, rms out {np.sqrt(np.mean(ref ** 2)):.3e}")
+    assert np.all(np.isfinite(got[a:b]))
+    assert err.max() <= ABS
+    assert np.all(got[:a] == SENTINEL) and np.all(got[b:] == SENTINEL)
+
+
+def test_gpu_linear_attention_ragged_segments():
+    _run([1, 63, 64, 65, 200], Hq=8, Hkv=2, seed=21)
+
+
+def test_gpu_linear_attention_strided_projection_rows():
+    _run([700, 303], Hq=4, Hkv=1, seed=22, lead=5, tail=7, strided=True)
+
+
+def test_gpu_linear_attention_llama_heads_long_segment():
+    _run([4100, 130], Hq=32, Hkv=8, seed=23, strided=True)

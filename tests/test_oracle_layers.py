@@ -72,3 +72,58 @@ def test_later_layer_flops_llama_shapes():
     assert per_row_macs == 218103808
     assert L.later_layer_flops(1) == 2 * per_row_macs
     assert L.later_layer_flops(1000) == 1000 * L.later_layer_flops(1)
+
+
+def _quadratic_linear_attention(q, k, v, cu):
+    """o_t = sum_{s<=t} w_ts v_s / sum_{s<=t} w_ts with w_ts = phi(q_t).phi(k_s),
+    the non-recurrent form, written with plain loops."""
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros_like(q)
+    for a, b in zip(cu[:-1], cu[1:]):
+        for t in range(a, b):
+            for h in range(Hq):
+                fq = L.feature_map(q[t, h])
+                num = np.zeros(D)
+                den = 0.0
+                for s in range(a, t + 1):
+                    w = math.fsum(fq * L.feature_map(k[s, h // G]))
+                    num += w * v[s, h // G]
+                    den += w
+                out[t, h] = num / den
+    return out
+
+
+def test_feature_map_closed_forms():
+    x = np.array([-50.0, -1.0, 0.0, 0.5, 3.0])
+    want = [math.exp(-50.0), math.exp(-1.0), 1.0, 1.5, 4.0]
+    assert np.allclose(L.feature_map(x), want, rtol=1e-15, atol=0)
+    assert np.all(L.feature_map(np.linspace(-700, 700, 101)) > 0)
+
+
+def test_linear_attention_matches_quadratic_form():
+    rng = np.random.default_rng(3)
+    cu = [0, 5, 6, 13]
+    q = rng.standard_normal((13, 4, 6))
+    k = rng.standard_normal((13, 2, 6))
+    v = rng.standard_normal((13, 2, 6))
+    got = L.linear_attention(q, k, v, cu)
+    assert np.allclose(got, _quadratic_linear_attention(q, k, v, cu), rtol=1e-12, atol=1e-13)
+
+
+def test_linear_attention_special_cases():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((7, 2, 5))
+    k = rng.standard_normal((7, 1, 5))
+    v = rng.standard_normal((7, 1, 5))
+    out = L.linear_attention(q, k, v, [0, 7])
+    # the first token of a segment sees only itself: o = v
+    assert np.allclose(out[0], v[0], rtol=1e-14, atol=1e-15)
+    # a value shared by every token comes back unchanged
+    vc = np.repeat(v[:1], 7, axis=0)
+    assert np.allclose(L.linear_attention(q, k, vc, [0, 7]), np.broadcast_to(vc, (7, 2, 5)),
+                       rtol=1e-13, atol=1e-14)
+    # segments do not see each other: packing equals running each alone
+    packed = L.linear_attention(q, k, v, [0, 3, 7])
+    assert np.array_equal(packed[:3], L.linear_attention(q[:3], k[:3], v[:3], [0, 3]))
+    assert np.array_equal(packed[3:], L.linear_attention(q[3:], k[3:], v[3:], [0, 4]))

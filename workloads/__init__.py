@@ -464,3 +464,12 @@ def linear_inputs(seed: int, rows: int, k: int, n: int, x_scale: float = 1.0):
     x = f32_to_bf16_bits(_normal32(rng, (rows, k), x_scale))
     w = f32_to_bf16_bits(_normal32(rng, (n, k), 1.0 / np.sqrt(k)))
     return x, w
+
+
+def attention_inputs(seed: int, rows: int, Hq: int, Hkv: int, D: int):
+    """q [rows, Hq, D], k and v [rows, Hkv, D] ~ N(0, 1), bf16 bits."""
+    rng = np.random.default_rng(seed)
+    q = f32_to_bf16_bits(_normal32(rng, (rows, Hq, D)))
+    k = f32_to_bf16_bits(_normal32(rng, (rows, Hkv, D)))
+    v = f32_to_bf16_bits(_normal32(rng, (rows, Hkv, D)))
+    return q, k, v
