@@ -139,10 +139,10 @@ up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const
                               void* out, void* stream) {
   if (!cu_seqlens || !q || !k || !v || !out)
     return fail(UP_ERR_INVALID, "cu_seqlens, q, k, v and out must be non-NULL");
-  if (num_seqs <= 0) return fail(UP_ERR_INVALID, "num_seqs must be >= 1 (got %d)", num_seqs);
-  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv || Hq > 65535)
-    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d), at most 65535", Hq,
-                Hkv);
+  if (num_seqs <= 0 || num_seqs > 65535)
+    return fail(UP_ERR_INVALID, "num_seqs must be in [1, 65535] (got %d)", num_seqs);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv)
+    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
   if (head_dim != 128) return fail(UP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
   if (q_stride < (int64_t)Hq * head_dim || k_stride < (int64_t)Hkv * head_dim ||
       v_stride < (int64_t)Hkv * head_dim || (q_stride | k_stride | v_stride) % 8)

@@ -11,7 +11,8 @@
 // tokens in order.
 //
 // Chunked form: the segment is walked in chunks of 64 tokens by one
-// workgroup per (segment, query head), four waves.  For chunk c with
+// workgroup per (segment, query head), four waves; the next chunk's rows
+// are loaded into registers while the current one is processed.  For chunk c with
 // states S, z of the chunks before it:
 //   A   = mask(phi(Q_c) phi(K_c)^T)           (64 x 64, key <= query)
 //   o_c = (A V_c + phi(Q_c) S) / (A 1 + phi(Q_c) z)
@@ -74,7 +75,7 @@ __device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b <<
 
 __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int s = blockIdx.x, h = blockIdx.y;
+  const int h = blockIdx.x, s = blockIdx.y;
   const int g = h / (a.Hq / a.Hkv);
   const int t_begin = a.cu_seqlens[s], t_end = a.cu_seqlens[s + 1];
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
@@ -91,25 +92,36 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
     for (int e = 0; e < 16; ++e) sacc[i][e] = 0.f;
   __syncthreads();
 
+  // the chunk's raw q, k, v rows: thread tid handles (row p / 16, 16-byte
+  // column chunk p % 16) for p = tid + 256 i; loaded one chunk ahead
+  u32x4 rq[4], rk[4], rv[4];
+  auto load_chunk = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + kThreads * i, r = p >> 4, c = p & 15;
+      rq[i] = rk[i] = rv[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t0 + r < t_end) {
+        const long t = t0 + r;
+        rq[i] = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
+        rk[i] = *(const u32x4*)(a.k + t * a.k_stride + (long)g * kD + c * 8);
+        rv[i] = *(const u32x4*)(a.v + t * a.v_stride + (long)g * kD + c * 8);
+      }
+    }
+  };
+  if (t_begin < t_end) load_chunk(t_begin);
+
   for (int t0 = t_begin; t0 < t_end; t0 += kC) {
     const int nrows = min(kC, t_end - t0);
     // (a) the chunk's phi(q), phi(k), v into LDS; rows past the segment are
     // zero (not phi(0)), so they add nothing to A, S or z
 #pragma unroll
-    for (int p = tid; p < kC * 16; p += kThreads) {
-      const int r = p >> 4, c = p & 15;
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + kThreads * i, r = p >> 4, c = p & 15;
       const bool ok = r < nrows;
-      u32x4 qr = {0u, 0u, 0u, 0u}, kr = qr, vr = qr;
-      if (ok) {
-        const long t = t0 + r;
-        qr = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
-        kr = *(const u32x4*)(a.k + t * a.k_stride + (long)g * kD + c * 8);
-        vr = *(const u32x4*)(a.v + t * a.v_stride + (long)g * kD + c * 8);
-      }
       bf16x8 fq, fk;
-      const uint16_t* q16 = (const uint16_t*)&qr;
-      const uint16_t* k16 = (const uint16_t*)&kr;
-      const uint16_t* v16 = (const uint16_t*)&vr;
+      const uint16_t* q16 = (const uint16_t*)&rq[i];
+      const uint16_t* k16 = (const uint16_t*)&rk[i];
+      const uint16_t* v16 = (const uint16_t*)&rv[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         fq[e] = ok ? (__bf16)phi(bf2f(q16[e])) : (__bf16)0.f;
@@ -123,21 +135,23 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
         *(uint16_t*)(lds + VT + off128(c * 8 + e, r)) = v16[e];
       }
     }
+    if (t0 + kC < t_end) load_chunk(t0 + kC);
     __syncthreads();
 
     // (b) wave w: A block (rows 32 (w >> 1).., keys 32 (w & 1)..), masked,
     // to LDS in bf16; and this chunk's phi(K)^T V into S (registers)
     {
       const int mr = w >> 1, nc = w & 1;
-      f32x16 acc;
+      f32x16 acc2[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc2[0][e] = acc2[1][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mr * 32 + l32, ks * 16 + hl * 8));
         const bf16x8 kb = *(lbf16x8*)(uintptr_t)(L0 + KF + off256(nc * 32 + l32, ks * 16 + hl * 8));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, acc, 0, 0, 0);
+        acc2[ks & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, acc2[ks & 1], 0, 0, 0);
       }
+      const f32x16 acc = acc2[0] + acc2[1];
       const int key = nc * 32 + l32;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
@@ -164,10 +178,19 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
       const int r = tid >> 2, x = tid & 3;
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) d += (float)*(const __bf16*)(lds + AB + off128(r, x * 16 + e));
-      const float* z = (const float*)(lds + ZF);
-#pragma unroll 8
-      for (int e = 0; e < 32; ++e) d += (float)*(const __bf16*)(lds + QF + off256(r, x * 32 + e)) * z[x * 32 + e];
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 av = *(const bf16x8*)(lds + AB + off128(r, x * 16 + j * 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += (float)av[e];
+      }
+      const float* z = (const float*)(lds + ZF) + x * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 qv = *(const bf16x8*)(lds + QF + off256(r, x * 32 + j * 8));
+        const float4 z0 = *(const float4*)(z + j * 8), z1 = *(const float4*)(z + j * 8 + 4);
+        d += (float)qv[0] * z0.x + (float)qv[1] * z0.y + (float)qv[2] * z0.z + (float)qv[3] * z0.w +
+             (float)qv[4] * z1.x + (float)qv[5] * z1.y + (float)qv[6] * z1.z + (float)qv[7] * z1.w;
+      }
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
       if (x == 0) ((float*)(lds + DN))[r] = d;
@@ -177,38 +200,45 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
     // (d) wave w: outputs of columns 32w.. for both 32-row blocks:
     // A V + phi(Q) (S_hi + S_lo), divided by the row's denominator
     {
+      f32x16 acc[2][2];  // [row block][A V + phi(Q) S_hi, phi(Q) S_lo]
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 acc;
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[mb][0][e] = acc[mb][1][e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
           const bf16x8 aa = *(lbf16x8*)(uintptr_t)(L0 + AB + off128(mb * 32 + l32, ks * 16 + hl * 8));
-          const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc, 0, 0, 0);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc[mb][0], 0, 0, 0);
         }
+      }
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 sh = *(lbf16x8*)(uintptr_t)(L0 + SH + off256(w * 32 + l32, ks * 16 + hl * 8));
+        const bf16x8 sl = *(lbf16x8*)(uintptr_t)(L0 + SL + off256(w * 32 + l32, ks * 16 + hl * 8));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
           const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mb * 32 + l32, ks * 16 + hl * 8));
-          const bf16x8 sh = *(lbf16x8*)(uintptr_t)(L0 + SH + off256(w * 32 + l32, ks * 16 + hl * 8));
-          const bf16x8 sl = *(lbf16x8*)(uintptr_t)(L0 + SL + off256(w * 32 + l32, ks * 16 + hl * 8));
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc, 0, 0, 0);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc[mb][1], 0, 0, 0);
         }
-        const float* den = (const float*)(lds + DN);
-        const int col = w * 32 + l32;
+      }
+      const float* den = (const float*)(lds + DN);
+      const int col = w * 32 + l32;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int row = mb * 32 + jj * 8 + hl * 4 + e;
             if (row < nrows) {
-              const float o = acc[jj * 4 + e] / den[row];
+              const float o = (acc[mb][0][jj * 4 + e] + acc[mb][1][jj * 4 + e]) / den[row];
               *(__bf16*)(a.out + ((long)(t0 + row) * a.Hq + h) * kD + col) = (__bf16)o;
             }
           }
-      }
     }
     __syncthreads();
 
@@ -229,11 +259,17 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
         *(bf16x4*)(lds + SH + off256(dout, din)) = hi;
         *(bf16x4*)(lds + SL + off256(dout, din)) = lo;
       }
-    if (tid < kD) {
+    {
+      const int d = tid >> 1, half = tid & 1;
       float zs = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < kC; ++e) zs += (float)*(const __bf16*)(lds + KT + off128(tid, e));
-      ((float*)(lds + ZF))[tid] += zs;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 kv = *(const bf16x8*)(lds + KT + off128(d, half * 32 + j * 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zs += (float)kv[e];
+      }
+      zs += __shfl_xor(zs, 1, 64);
+      if (half == 0) ((float*)(lds + ZF))[d] += zs;
     }
     __syncthreads();
   }
@@ -258,7 +294,9 @@ hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void*
   hipError_t e = hipFuncSetAttribute((const void*)linear_attn_bf16_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(linear_attn_bf16_kernel, dim3(S, Hq), dim3(kThreads), kLdsBytes, st, a);
+  // heads fastest: the workgroups of one segment go out together, and a
+  // compute unit that finishes a short segment takes the next one's
+  hipLaunchKernelGGL(linear_attn_bf16_kernel, dim3(Hq, S), dim3(kThreads), kLdsBytes, st, a);
   return hipGetLastError();
 }
 

@@ -250,7 +250,8 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
  * strides in elements, multiples of 8, so the q, k and v column ranges of
  * one [rows, (Hq + 2 Hkv) * head_dim] projection output can be passed
  * directly), 16-byte aligned.  out: [rows, Hq, head_dim] bf16; rows outside
- * the segments are not written.  head_dim must be 128 (UP_ERR_UNSUPPORTED).
+ * the segments are not written.  head_dim must be 128 (UP_ERR_UNSUPPORTED);
+ * num_seqs at most 65535.
  * Device precondition: cu_seqlens non-decreasing.
  */
 up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,

@@ -186,6 +186,7 @@ def test_linear_attention_argument_validation(L):
     assert la(cu=None) == UP_ERR_INVALID
     assert la(out=None) == UP_ERR_INVALID
     assert la(S=0) == UP_ERR_INVALID
+    assert la(S=65536) == UP_ERR_INVALID
     assert la(Hq=30) == UP_ERR_INVALID
     assert la(D=64) == UP_ERR_UNSUPPORTED
     assert la(qs=4000) == UP_ERR_INVALID  # cannot hold 32 heads of 128
