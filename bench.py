@@ -720,6 +720,25 @@ def main():
     res["roofline"]["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOP/s"]
     res["attainable_peaks"] = att
     res["compact_hbm"]["frac_of_attainable"] = res["compact_hbm"]["GB/s"] / att["hbm_copy_GB/s"]
+    # every pass against the HBM roofline, with its algorithmic bytes: the
+    # rotary/cache-write pass reads k, v and writes both to the cache (plus
+    # position and slot per token; the plan and block-mass kernels launched
+    # with it move a few MB); scores read the block mass and write one float
+    # per block; top-p reads the scores and writes a keep byte per block
+    # (plus per-segment counts); compaction as above
+    S = len(call.segments)
+    e_b = 2
+    pass_bytes = {
+        "rope_kv_plan_mass": (T * (4 * wl.Hkv * wl.D * e_b + 8), float(st_mean[0]) - attn_ms),
+        "scores": (4 * wl.Hq * nb + 4 * nb, float(st_mean[1])),
+        "select": (5 * nb + 4 * S, float(st_mean[2])),
+        "compact": (compact_bytes, float(st_mean[3])),
+    }
+    res["passes_hbm"] = {
+        k: {"us": ms * 1e3, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
+            "frac": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "frac_of_attainable": b / (ms * 1e-3) / 1e9 / att["hbm_copy_GB/s"]}
+        for k, (b, ms) in pass_bytes.items()}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
