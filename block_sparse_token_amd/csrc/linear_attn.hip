@@ -11,17 +11,18 @@
 // tokens in order.
 //
 // Chunked form: the segment is walked in chunks of 64 tokens by one
-// workgroup per (segment, query head), four waves; the next chunk's rows
-// are loaded into registers while the current one is processed.  For chunk c with
+// workgroup per (segment, query head), four waves, two workgroups per
+// compute unit.  For chunk c with
 // states S, z of the chunks before it:
 //   A   = mask(phi(Q_c) phi(K_c)^T)           (64 x 64, key <= query)
 //   o_c = (A V_c + phi(Q_c) S) / (A 1 + phi(Q_c) z)
 //   S  += phi(K_c)^T V_c,   z += phi(K_c)^T 1
 // All four products run on v_mfma_f32_32x32x16_bf16.  S stays in float32
-// registers (wave w owns output columns 32w..32w+31); for the product
-// phi(Q_c) S it is handed over in LDS as the bf16 pair hi + lo (hi the
-// rounding of S, lo that of the remainder), so S enters with about 16
-// significant bits.  The denominators use the same bf16 A and phi(K) as the
+// registers (wave w owns output columns 32w..32w+31, which are the columns
+// of the outputs it computes); the product phi(Q_c) S takes it from there
+// as the bf16 pair hi + lo (hi the rounding of S, lo that of the
+// remainder), so S enters with about 16 significant bits.  With no copy of
+// S in LDS, two workgroups share a compute unit.  The denominators use the same bf16 A and phi(K) as the
 // numerators.  LDS tiles are row-major with 16-byte chunks XOR-swizzled per
 // row, so fragment reads of 16 rows fall on distinct banks; phi(K) and V
 // are also stored transposed (key-minor), which is the layout the products
@@ -47,12 +48,10 @@ constexpr int KF = QF + kC * kD * 2;   // phi(K) [64][128]
 constexpr int KT = KF + kC * kD * 2;   // phi(K)^T [128][64] rows of 128 B
 constexpr int VT = KT + kD * kC * 2;   // V^T [128][64]
 constexpr int AB = VT + kD * kC * 2;   // A [64][64]         rows of 128 B
-constexpr int SH = AB + kC * kC * 2;   // S^T hi [128][128]   rows of 256 B
-constexpr int SL = SH + kD * kD * 2;   // S^T lo
-constexpr int ZF = SL + kD * kD * 2;   // z [128] f32
+constexpr int ZF = AB + kC * kC * 2;   // z [128] f32
 constexpr int DN = ZF + kD * 4;        // denominators [64] f32
 constexpr int kLdsBytes = DN + kC * 4;
-static_assert(kLdsBytes <= 160 * 1024, "LDS");
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per compute unit");
 
 // byte offset of element (r, e) in a row-major bf16 tile with 256-byte rows
 __device__ inline int off256(int r, int e) { return r * 256 + ((((e >> 3) ^ (r & 15))) << 4) + (e & 7) * 2; }
@@ -73,7 +72,7 @@ struct LinAttnArgs {
 
 __device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int h = blockIdx.x, s = blockIdx.y;
   const int g = h / (a.Hq / a.Hkv);
@@ -82,9 +81,8 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t L0 = lds_addr_of(lds);
 
-  // S^T hi/lo and z start at zero
-  for (int i = tid; i < (2 * kD * kD * 2 + kD * 4) / 16; i += kThreads)
-    *(u32x4*)(lds + SH + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  // z starts at zero
+  if (tid < kD * 4 / 16) *(u32x4*)(lds + ZF + tid * 16) = u32x4{0u, 0u, 0u, 0u};
   f32x16 sacc[4];  // S[32i + row][32w + col] blocks, i = d_in block
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -93,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
   __syncthreads();
 
   // the chunk's raw q, k, v rows: thread tid handles (row p / 16, 16-byte
-  // column chunk p % 16) for p = tid + 256 i; loaded one chunk ahead
+  // column chunk p % 16) for p = tid + 256 i
   u32x4 rq[4], rk[4], rv[4];
   auto load_chunk = [&](int t0) {
 #pragma unroll
@@ -108,10 +106,10 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
       }
     }
   };
-  if (t_begin < t_end) load_chunk(t_begin);
 
   for (int t0 = t_begin; t0 < t_end; t0 += kC) {
     const int nrows = min(kC, t_end - t0);
+    load_chunk(t0);
     // (a) the chunk's phi(q), phi(k), v into LDS; rows past the segment are
     // zero (not phi(0)), so they add nothing to A, S or z
 #pragma unroll
@@ -135,11 +133,10 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
         *(uint16_t*)(lds + VT + off128(c * 8 + e, r)) = v16[e];
       }
     }
-    if (t0 + kC < t_end) load_chunk(t0 + kC);
     __syncthreads();
 
     // (b) wave w: A block (rows 32 (w >> 1).., keys 32 (w & 1)..), masked,
-    // to LDS in bf16; and this chunk's phi(K)^T V into S (registers)
+    // to LDS in bf16
     {
       const int mr = w >> 1, nc = w & 1;
       f32x16 acc2[2];
@@ -160,15 +157,6 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
           const int row = mr * 32 + jj * 8 + hl * 4 + e;
           *(__bf16*)(lds + AB + off128(row, key)) = (__bf16)(key <= row ? acc[jj * 4 + e] : 0.f);
         }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x8 ka = *(lbf16x8*)(uintptr_t)(L0 + KT + off128(i * 32 + l32, ks * 16 + hl * 8));
-          sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, sacc[i], 0, 0, 0);
-        }
-      }
     }
     __syncthreads();
 
@@ -198,31 +186,46 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
     __syncthreads();
 
     // (d) wave w: outputs of columns 32w.. for both 32-row blocks:
-    // A V + phi(Q) (S_hi + S_lo), divided by the row's denominator
+    // A V + phi(Q) S, divided by the row's denominator.  S comes from this
+    // wave's own registers: for the 16 rows of step ks, lane (c, half 0)
+    // holds rows 8jj + 0..3 of column c and lane (c, half 1) rows 8jj +
+    // 4..7; one v_permlane32_swap per register pair gives each lane the 8
+    // consecutive rows the product reads, split into bf16 hi + lo.
     {
-      f32x16 acc[2][2];  // [row block][A V + phi(Q) S_hi, phi(Q) S_lo]
+      f32x16 acc[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][0][e] = acc[mb][1][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const bf16x8 aa = *(lbf16x8*)(uintptr_t)(L0 + AB + off128(mb * 32 + l32, ks * 16 + hl * 8));
-          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc[mb][0], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc[mb], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 sh = *(lbf16x8*)(uintptr_t)(L0 + SH + off256(w * 32 + l32, ks * 16 + hl * 8));
-        const bf16x8 sl = *(lbf16x8*)(uintptr_t)(L0 + SL + off256(w * 32 + l32, ks * 16 + hl * 8));
+        const int i = ks >> 1, j0 = (ks & 1) * 2;
+        bf16x8 sh, sl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sacc[i][j0 * 4 + e]),
+                                                          __float_as_uint(sacc[i][j0 * 4 + 4 + e]),
+                                                          false, false);
+          const float lo_rows = __uint_as_float(r[0]), hi_rows = __uint_as_float(r[1]);
+          sh[e] = (__bf16)lo_rows;
+          sl[e] = (__bf16)(lo_rows - (float)sh[e]);
+          sh[4 + e] = (__bf16)hi_rows;
+          sl[4 + e] = (__bf16)(hi_rows - (float)sh[4 + e]);
+        }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mb * 32 + l32, ks * 16 + hl * 8));
-          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc[mb][0], 0, 0, 0);
-          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc[mb][1], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc[mb], 0, 0, 0);
         }
       }
       const float* den = (const float*)(lds + DN);
@@ -235,30 +238,23 @@ __global__ __launch_bounds__(kThreads) void linear_attn_bf16_kernel(LinAttnArgs 
           for (int e = 0; e < 4; ++e) {
             const int row = mb * 32 + jj * 8 + hl * 4 + e;
             if (row < nrows) {
-              const float o = (acc[mb][0][jj * 4 + e] + acc[mb][1][jj * 4 + e]) / den[row];
+              const float o = acc[mb][jj * 4 + e] / den[row];
               *(__bf16*)(a.out + ((long)(t0 + row) * a.Hq + h) * kD + col) = (__bf16)o;
             }
           }
     }
-    __syncthreads();
 
-    // (e) hand S over for the next chunk (hi + lo, transposed), and add this
-    // chunk's keys to z
+    // (e) this chunk's phi(K)^T V into S (registers; wave w's columns), and
+    // its keys into z once every wave has read z for the denominators
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = sacc[i][jj * 4 + e];
-          hi[e] = (__bf16)x;
-          lo[e] = (__bf16)(x - (float)hi[e]);
-        }
-        const int dout = w * 32 + l32, din = i * 32 + jj * 8 + hl * 4;
-        *(bf16x4*)(lds + SH + off256(dout, din)) = hi;
-        *(bf16x4*)(lds + SL + off256(dout, din)) = lo;
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 ka = *(lbf16x8*)(uintptr_t)(L0 + KT + off128(i * 32 + l32, ks * 16 + hl * 8));
+        sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, sacc[i], 0, 0, 0);
       }
+    }
     {
       const int d = tid >> 1, half = tid & 1;
       float zs = 0.f;
