@@ -68,3 +68,32 @@ def test_gpu_linear_attention_strided_projection_rows():
 
 def test_gpu_linear_attention_llama_heads_long_segment():
     _run([4100, 130], Hq=32, Hkv=8, seed=23, strided=True)
+
+
+def test_gpu_linear_attention_headline_batch_sampled_segments():
+    """The launch the propagation benchmark times: 16 segments of lengths
+    uniform in [512, 8192], 32 / 8 heads, q, k, v as column ranges of one
+    projection output (drawn on the device with torch's seeded generator).
+    The oracle recomputes three whole segments (the longest among them)."""
+    Hq, Hkv, D = 32, 8, 128
+    lengths = [int(x) for x in np.random.default_rng(2).integers(512, 8193, size=16)]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rows = int(cu[-1])
+    log(f"linear attention headline-size batch rows={rows} segments={len(lengths)}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    qkv = torch.randn((rows, (Hq + 2 * Hkv) * D), generator=g, device="cuda").to(torch.bfloat16)
+    q = qkv[:, : Hq * D].view(rows, Hq, D)
+    k = qkv[:, Hq * D: (Hq + Hkv) * D].view(rows, Hkv, D)
+    v = qkv[:, (Hq + Hkv) * D:].view(rows, Hkv, D)
+    out = torch.full((rows, Hq, D), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    Bd.up_linear_attn_bf16(torch.from_numpy(cu).cuda(), q, k, v, out)
+    torch.cuda.synchronize()
+    longest = int(np.argmax(lengths))
+    for s in sorted({0, longest, len(lengths) - 1}):
+        a, b = int(cu[s]), int(cu[s + 1])
+        ref = oracle.linear_attention(_f64(q[a:b]), _f64(k[a:b]), _f64(v[a:b]), [0, b - a])
+        err = float(np.abs(_f64(out[a:b]) - ref).max())
+        log(f"  segment {s} ({b - a} tokens): max abs err {err:.3e}")
+        assert err <= ABS
+    assert not bool((out == SENTINEL).any()), "a row inside the segments was not written"
