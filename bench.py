@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="throughput against the number of packed prompts, and packed vs "
                          "bin-packed rows vs padded layouts of the headline batch")
+    ap.add_argument("--p", type=float, default=None,
+                    help="with --propagation: top-p of the selection instead of the workload's "
+                         "0.95 (shows how the later-layer saving follows the kept fraction)")
     ap.add_argument("--propagation", action="store_true",
                     help="time one later layer's linear maps on all vs the kept tokens of the "
                          "headline batch")
@@ -295,9 +298,10 @@ def attainable_peaks(torch, B, stream):
                       "up_peak_copy (1 GiB read + 1 GiB written), medians of event-timed launches"}
 
 
-def headline_call(torch):
+def headline_call(torch, p=None):
     """The headline workload's one call, staged on the GPU: inputs, caches,
-    batch metadata, and the hidden states, positions and KV slots to compact."""
+    batch metadata, and the hidden states, positions and KV slots to compact
+    (top-p ``p`` instead of the workload's when given)."""
     import workloads as W
     from block_sparse_token_amd import step as ST
 
@@ -315,7 +319,8 @@ def headline_call(torch):
                         k=ST.stored_to_tensor(call.k, dev), v=ST.stored_to_tensor(call.v, dev),
                         k_cache=kc, v_cache=vc, num_blocks=call.num_blocks(wl.block_size),
                         flags=torch.from_numpy(call.flags.astype(np.uint8)).to(dev),
-                        block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, rows=rows)
+                        block_size=wl.block_size, p=wl.p if p is None else p,
+                        rope_theta=wl.theta, rows=rows)
     return wl, call, pc
 
 
@@ -371,7 +376,7 @@ def run_propagation(args):
     from block_sparse_token_amd import binding as B
     from oracle.prefill import default_threads
 
-    wl, call, pc = headline_call(torch)
+    wl, call, pc = headline_call(torch, args.p)
     pc.launch()
     torch.cuda.synchronize()
     T = call.T
@@ -459,7 +464,7 @@ def run_propagation(args):
         "config": {"workload": "one Llama-3.1-8B-shaped later linear-attention layer (4096 -> 6144, "
                                "causal linear attention 32/8 heads x 128, 4096 -> 4096, SwiGLU "
                                "4096 -> 2 x 14336, 14336 -> 4096) on the packed prefill of "
-                               f"{T} tokens, {kept} kept by top-p 0.95 (block 64)",
+                               f"{T} tokens, {kept} kept by top-p {pc.p} (block 64)",
                    "rows_all": T, "rows_kept": kept},
         "layer_ms_all": wall_all, "layer_ms_kept": wall_kept,
         "time_saved_frac": 1.0 - wall_kept / wall_all,
