@@ -168,6 +168,9 @@ up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap
     return fail(UP_ERR_INVALID, "act must be UP_ACT_NONE or UP_ACT_SWIGLU (got %d)", act);
   if ((double)rows_cap * k_in * 2 >= 4294967296.0 || (double)n_out * k_in * 2 >= 4294967296.0)
     return fail(UP_ERR_UNSUPPORTED, "x and w must each be under 4 GiB (32-bit row offsets)");
+  // one workgroup per 256 x 256 output tile (plus at most 7 x 32 idle ones)
+  if ((double)((rows_cap + 255) / 256) * (n_out / 256) + 224.0 >= 2147483648.0)
+    return fail(UP_ERR_UNSUPPORTED, "more than 2^31 output tiles");
   if ((((uintptr_t)x) | ((uintptr_t)w)) & 15)
     return fail(UP_ERR_INVALID, "x and w must be 16-byte aligned");
   if (((uintptr_t)y) & 7) return fail(UP_ERR_INVALID, "y must be 8-byte aligned");

@@ -176,6 +176,9 @@ def test_linear_argument_validation(L):
     assert lin(y=ctypes.c_void_p(0x1004)) == UP_ERR_INVALID  # not 8-byte aligned
     assert lin(rows=1 << 20, k=4096) == UP_ERR_UNSUPPORTED  # x of 8 GiB: 32-bit offsets
     assert "4 GiB" in L.up_last_error().decode()
+    # each operand under 4 GiB, but more output tiles than one launch takes
+    assert lin(rows=(1 << 25) - 1, n=(1 << 25) - 256, k=64) == UP_ERR_UNSUPPORTED
+    assert "tiles" in L.up_last_error().decode()
 
 
 def test_linear_attention_argument_validation(L):
