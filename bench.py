@@ -239,12 +239,16 @@ def run_other_workload(args):
 
 
 def kernel_code_hash(path):
-    """sha256 of a source file with its comments and whitespace removed, so
-    that a profile stays matched to a kernel whose comments were edited."""
+    """sha256 of a source file with its comments and whitespace removed, and
+    of the file's own compile flags when it has any, so that a profile stays
+    matched to a kernel whose comments were edited and to no other build."""
+    from block_sparse_token_amd.build import FILE_FLAGS
     txt = open(path).read()
     txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
     txt = re.sub(r"//[^\n]*", " ", txt)
-    return hashlib.sha256(" ".join(txt.split()).encode()).hexdigest()
+    flags = FILE_FLAGS.get(os.path.basename(path), [])
+    key = " ".join(txt.split()) + (" | " + " ".join(flags) if flags else "")
+    return hashlib.sha256(key.encode()).hexdigest()
 
 
 def traffic_from_profile(src_hash, name="attn_bf16_packed_llama8b_counters.md"):

@@ -31,9 +31,18 @@ COMMON = [
 ]
 
 
+# Instruction scheduling per file, chosen by timing both on one GPU: the
+# maximum-ILP strategy makes the attention sweep 2% and the linear-attention
+# chunk loop 16% faster, and the later-layer GEMM 3-4% slower.
+FILE_FLAGS = {
+    "attn_bf16.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+    "linear_attn.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
                os.path.join(CSRC, src), "-o", obj]

@@ -46,3 +46,14 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_kernel_hash_covers_the_files_compile_flags(tmp_path):
+    """A profile taken on a build with other per-file compile flags (the
+    instruction schedule changes the machine code) does not match."""
+    from block_sparse_token_amd.build import FILE_FLAGS
+    src = os.path.join(ROOT, "block_sparse_token_amd", "csrc", "attn_bf16.hip")
+    assert FILE_FLAGS.get("attn_bf16.hip")
+    copy = tmp_path / "same_source_no_flags.hip"
+    copy.write_text(open(src).read())
+    assert bench.kernel_code_hash(src) != bench.kernel_code_hash(str(copy))
