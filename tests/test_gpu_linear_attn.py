@@ -62,6 +62,11 @@ def test_gpu_linear_attention_ragged_segments():
     _run([1, 63, 64, 65, 200], Hq=8, Hkv=2, seed=21)
 
 
+def test_gpu_linear_attention_empty_segments_and_single_head_groups():
+    # segments of no tokens, and one query head per KV head
+    _run([0, 70, 0, 1, 129, 0], Hq=2, Hkv=2, seed=24)
+
+
 def test_gpu_linear_attention_strided_projection_rows():
     _run([700, 303], Hq=4, Hkv=1, seed=22, lead=5, tail=7, strided=True)
 
