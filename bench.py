@@ -748,6 +748,39 @@ def main():
             "frac": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "frac_of_attainable": b / (ms * 1e-3) / 1e9 / att["hbm_copy_GB/s"]}
         for k, (b, ms) in pass_bytes.items()}
+    # the same passes with the 256 MB Infinity Cache flushed before every
+    # step (a 512 MiB buffer written in between, outside the timed stages),
+    # so no pass finds its inputs in that cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    fl_ev = []
+    for i in range(min(K, 10)):
+        flush.fill_(i & 255)
+        e = [ev() for _ in range(5)]
+        a_ev = (ev(), ev())
+        B.up_profile_attn_events(*a_ev)
+        e[0].record(stream)
+        pc.attention()
+        e[1].record(stream)
+        pc.scores_stage()
+        e[2].record(stream)
+        pc.select_stage()
+        e[3].record(stream)
+        pc.compact_stage()
+        e[4].record(stream)
+        fl_ev.append((e, a_ev))
+    torch.cuda.synchronize()
+    B.up_profile_attn_events()
+    del flush
+    st_fl = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e, _ in fl_ev]).mean(axis=0)
+    attn_fl = float(np.mean([a.elapsed_time(b) for _, (a, b) in fl_ev]))
+    fl_ms = {"rope_kv_plan_mass": float(st_fl[0]) - attn_fl, "scores": float(st_fl[1]),
+             "select": float(st_fl[2]), "compact": float(st_fl[3])}
+    for k, (b, _) in pass_bytes.items():
+        res["passes_hbm"][k].update({"us_cache_flushed": fl_ms[k] * 1e3,
+                                     "GB/s_cache_flushed": b / (fl_ms[k] * 1e-3) / 1e9,
+                                     "frac_cache_flushed": b / (fl_ms[k] * 1e-3) / 1e9 /
+                                     PEAK_HBM_GBS})
+    res["roofline"]["avg_ms_cache_flushed"] = attn_fl
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
