@@ -5,6 +5,7 @@ from .prefill import (  # noqa: F401
     attention,
     block_mass,
     compact,
+    kept_cache_positions,
     normalise_scores,
     num_blocks,
     p_fixed_point,

@@ -178,7 +178,7 @@ def num_blocks(n: int, B: int) -> int:
     return -(-n // B)
 
 
-def block_mass(q_rot, keys, q_pos, k_pos, n_ctx, n, B, window=0, scale=None):
+def block_mass(q_rot, keys, q_pos, k_pos, n_ctx, n, B, window=0, scale=None, scope="segment"):
     """Mass m_k per own block of a segment (float64 [nb]).
 
     The segment's rows are local [0, n); its keys are ``n_ctx`` cached keys
@@ -187,11 +187,30 @@ def block_mass(q_rot, keys, q_pos, k_pos, n_ctx, n, B, window=0, scale=None):
     row t of that block, the exact softmax probabilities over all visible keys
     (cached ones included, so they take part in the normaliser) are summed
     over the own keys of each block.  Cached keys are not scored.
+
+    scope="prompt" (whole-prompt scoring of a prompt's final chunk): the
+    blocks are those of the whole prompt, B keys each from its first key,
+    over the n_ctx cached keys and the n own ones, so cached blocks are
+    scored too; n_ctx must be a multiple of B, which makes the prompt's last
+    block the segment's last block (the same query rows).
     """
     Hq = q_rot.shape[1]
     G = Hq // keys.shape[1]
     nb = num_blocks(n, B)
     r0 = (nb - 1) * B
+    if scope == "prompt":
+        if n_ctx % B:
+            raise ValueError("whole-prompt scoring needs the cached length to be a multiple of B")
+        nbp = num_blocks(n_ctx + n, B)
+        m = np.zeros(nbp, np.float64)
+        for h in range(Hq):
+            P, _ = softmax_probs(q_rot[r0:n], keys, q_pos[r0:n], k_pos, window, h, G, scale)
+            per_key = P.sum(axis=0)  # [n_ctx + n], keys in position order
+            for kb in range(nbp):
+                m[kb] += per_key[kb * B : min((kb + 1) * B, n_ctx + n)].sum()
+        return m
+    if scope != "segment":
+        raise ValueError(f"unknown scope {scope!r}")
     m = np.zeros(nb, np.float64)
     for h in range(Hq):
         P, _ = softmax_probs(q_rot[r0:n], keys, q_pos[r0:n], k_pos, window, h, G, scale)
@@ -273,7 +292,7 @@ def topp_select(scores32: np.ndarray, p: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def compact(cu_seqlens, flags, block_size, keep_blocks, rows=None):
+def compact(cu_seqlens, flags, block_size, keep_blocks, rows=None, ctx=None, scope="segment"):
     """Compaction of the kept tokens.
 
     Token t of segment s is kept when s is not scored, or when its block
@@ -282,6 +301,11 @@ def compact(cu_seqlens, flags, block_size, keep_blocks, rows=None):
     Returns index_map (ascending original packed indices), cu_seqlens_out
     (per-segment kept counts, prefix-summed) and each row tensor of ``rows``
     gathered by index_map (byte-exact copies).
+
+    scope="prompt": the blocks of a scored segment are those of its whole
+    prompt (``ctx[s]`` cached tokens, a multiple of block_size, then its
+    own), so own token i is kept when prompt block (ctx[s] + i) //
+    block_size is; use ``kept_cache_positions`` for the cached tokens.
     """
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     S = len(cu) - 1
@@ -290,7 +314,8 @@ def compact(cu_seqlens, flags, block_size, keep_blocks, rows=None):
         n = int(cu[s + 1] - cu[s])
         if flags[s]:
             kb = np.asarray(keep_blocks[s], bool)
-            keep_tok.append(np.repeat(kb, block_size)[:n])
+            c0 = int(ctx[s]) if scope == "prompt" else 0
+            keep_tok.append(np.repeat(kb, block_size)[c0 : c0 + n])
         else:
             keep_tok.append(np.ones(n, bool))
     kt = np.concatenate(keep_tok) if keep_tok else np.zeros(0, bool)
@@ -301,6 +326,21 @@ def compact(cu_seqlens, flags, block_size, keep_blocks, rows=None):
     for name, r in (rows or {}).items():
         out_rows[name] = np.asarray(r)[index_map]
     return index_map, cu_out, out_rows
+
+
+def kept_cache_positions(flags, block_size, keep_blocks, ctx):
+    """Whole-prompt scoring: per scored segment, the positions of its cached
+    tokens whose prompt block is kept (ascending); empty for unscored
+    segments.  The later layers attend to these cached keys only."""
+    out = []
+    for s, f in enumerate(flags):
+        if not f:
+            out.append(np.zeros(0, np.int64))
+            continue
+        kb = np.asarray(keep_blocks[s], bool)
+        u = np.arange(int(ctx[s]), dtype=np.int64)
+        out.append(u[kb[u // block_size]])
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -345,7 +385,7 @@ class KVCacheModel:
 
 def run_call(*, segments, q, k, v, positions, cu_seqlens, Hq, Hkv, D, theta, window,
              block_size, p, cache: KVCacheModel, rows=None, score=True, select=True,
-             threads=None, update_cache=True):
+             threads=None, update_cache=True, scope="segment"):
     """Everything one operator call computes, in order.
 
     ``segments``: list of (prompt_id, ctx, n, flagged).  q [T, Hq, D],
@@ -372,7 +412,7 @@ def run_call(*, segments, q, k, v, positions, cu_seqlens, Hq, Hkv, D, theta, win
         o, l = attention(q_rot, keys, vals, pos, k_pos, window, threads=threads)
         out[a:b], lse[a:b] = o, l
         if flagged and score:
-            m = block_mass(q_rot, keys, pos, k_pos, ctx, n, block_size, window)
+            m = block_mass(q_rot, keys, pos, k_pos, ctx, n, block_size, window, scope=scope)
             s32 = normalise_scores(m).astype(np.float32)
             masses.append(m)
             scores.append(s32)
@@ -388,6 +428,9 @@ def run_call(*, segments, q, k, v, positions, cu_seqlens, Hq, Hkv, D, theta, win
     res = {"out": out, "lse": lse, "mass": masses, "scores": scores, "keep": keeps}
     if score and select:
         flags = [bool(sg[3]) for sg in segments]
-        im, cu_out, rows_out = compact(cu, flags, block_size, keeps, rows)
+        ctxs = [int(sg[1]) for sg in segments]
+        im, cu_out, rows_out = compact(cu, flags, block_size, keeps, rows, ctx=ctxs, scope=scope)
         res.update(index_map=im, cu_seqlens_out=cu_out, rows_out=rows_out)
+        if scope == "prompt":
+            res["kept_cache_positions"] = kept_cache_positions(flags, block_size, keeps, ctxs)
     return res

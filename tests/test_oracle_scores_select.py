@@ -316,3 +316,60 @@ def test_layer2_runs_on_compacted_tokens():
     for i in range(2):
         t0 = cu[i]
         assert np.allclose(l2["out"][t0, 0], v2[im[t0], 0], atol=1e-14)
+
+
+def _prompt(rng, n, Hq=4, Hkv=2, D=32):
+    return (rng.standard_normal((n, Hq, D)), rng.standard_normal((n, Hkv, D)),
+            rng.standard_normal((n, Hkv, D)))
+
+
+def test_whole_prompt_scores_of_final_chunk_equal_one_pass():
+    """Chunked prefill equals one pass (glossary, How chunked prefill
+    works), so the final chunk's whole-prompt block masses, selection and
+    kept tokens (cached ones listed by position, own ones compacted) equal
+    those of the whole prompt scored in one call."""
+    rng = np.random.default_rng(11)
+    n_total, chunk, B, Hq, Hkv, D = 600, 256, 64, 4, 2, 32
+    q, k, v = _prompt(rng, n_total, Hq, Hkv, D)
+    pos = np.arange(n_total)
+    kw = dict(Hq=Hq, Hkv=Hkv, D=D, theta=500000.0, window=0, block_size=B, p=0.6)
+    one = oracle.run_call(segments=[(0, 0, n_total, True)], q=q, k=k, v=v, positions=pos,
+                          cu_seqlens=[0, n_total], cache=oracle.KVCacheModel(), **kw)
+    cache = oracle.KVCacheModel()
+    for c0 in range(0, n_total, chunk):
+        n = min(chunk, n_total - c0)
+        last = c0 + n == n_total
+        res = oracle.run_call(segments=[(0, c0, n, last)], q=q[c0:c0 + n], k=k[c0:c0 + n],
+                              v=v[c0:c0 + n], positions=pos[c0:c0 + n], cu_seqlens=[0, n],
+                              cache=cache, scope="prompt", **kw)
+    assert len(res["mass"][0]) == len(one["mass"][0]) == 10
+    assert np.allclose(res["mass"][0], one["mass"][0], rtol=1e-12, atol=0)
+    assert np.array_equal(res["keep"][0], one["keep"][0])
+    assert 0 < res["keep"][0].sum() < 10
+    kept = np.concatenate([res["kept_cache_positions"][0], c0 + res["index_map"]])
+    assert np.array_equal(kept, one["index_map"])
+
+
+def test_whole_prompt_scope_without_cache_equals_segment_scope():
+    rng = np.random.default_rng(12)
+    q, k, v = _prompt(rng, 150)
+    kw = dict(segments=[(0, 0, 150, True)], q=q, k=k, v=v, positions=np.arange(150),
+              cu_seqlens=[0, 150], Hq=4, Hkv=2, D=32, theta=0.0, window=0, block_size=32, p=0.7)
+    a = oracle.run_call(cache=oracle.KVCacheModel(), **kw)
+    b = oracle.run_call(cache=oracle.KVCacheModel(), scope="prompt", **kw)
+    assert np.array_equal(a["mass"][0], b["mass"][0])
+    assert np.array_equal(a["index_map"], b["index_map"])
+    assert len(b["kept_cache_positions"][0]) == 0
+
+
+def test_whole_prompt_scope_needs_block_aligned_cache():
+    rng = np.random.default_rng(13)
+    q, k, v = _prompt(rng, 40)
+    cache = oracle.KVCacheModel()
+    kw = dict(Hq=4, Hkv=2, D=32, theta=0.0, window=0, block_size=16, p=0.9)
+    oracle.run_call(segments=[(0, 0, 20, False)], q=q[:20], k=k[:20], v=v[:20],
+                    positions=np.arange(20), cu_seqlens=[0, 20], cache=cache, **kw)
+    with pytest.raises(ValueError):
+        oracle.run_call(segments=[(0, 20, 20, True)], q=q[20:], k=k[20:], v=v[20:],
+                        positions=np.arange(20, 40), cu_seqlens=[0, 20], cache=cache,
+                        scope="prompt", **kw)
