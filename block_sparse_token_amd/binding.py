@@ -17,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libuniprefill.so")
 
 UP_F32, UP_BF16 = 0, 1
+UP_SCOPE_SEGMENT, UP_SCOPE_PROMPT = 0, 1
 _DT = {torch.float32: UP_F32, torch.bfloat16: UP_BF16}
 
 c_i32, c_size, c_vp, c_f32, c_f64 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
@@ -58,11 +59,11 @@ def lib():
         sig = {
             "up_last_error": (ctypes.c_char_p, []),
             "up_version": (ctypes.c_char_p, []),
-            "up_block_offsets": (c_i32, [bp, c_i32, c_vp, c_vp]),
-            "up_attn_workspace_bytes": (c_size, [bp, c_i32, c_i32, c_i32, c_i32, c_i32]),
+            "up_block_offsets": (c_i32, [bp, c_i32, c_vp, c_i32, c_vp, c_vp]),
+            "up_attn_workspace_bytes": (c_size, [bp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
             "up_prefill_attn": (c_i32, [bp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
-                                        c_vp, c_f32, c_i32, c_f32, c_vp, c_i32, c_vp, c_vp, c_vp,
-                                        c_vp, c_vp, c_size, c_vp]),
+                                        c_vp, c_f32, c_i32, c_f32, c_vp, c_i32, c_i32, c_vp, c_vp,
+                                        c_vp, c_vp, c_vp, c_size, c_vp]),
             "up_block_scores": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
             "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
@@ -74,8 +75,10 @@ def lib():
                                             ctypes.c_int64, c_vp, ctypes.c_int64, c_i32, c_i32,
                                             c_i32, c_vp, c_vp]),
             "up_linear_bf16": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_vp]),
-            "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_i32,
+            "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+            "up_kept_cache_slots": (c_i32, [bp, c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp,
+                                            c_vp, c_vp, c_size, c_vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -88,7 +91,7 @@ def lib():
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
-            "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16"]
+            "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16", "up_kept_cache_slots"]
 
 
 def _check(st: int, what: str):
@@ -144,26 +147,31 @@ def up_version() -> str:
     return lib().up_version().decode()
 
 
-def up_block_offsets(batch: Batch, block_size: int, cu_blocks, stream=None):
-    _check(lib().up_block_offsets(batch.ref, block_size, _p(cu_blocks), _stream(stream)),
-           "up_block_offsets")
+def up_block_offsets(batch: Batch, block_size: int, cu_blocks, score_flags=None,
+                     score_scope=UP_SCOPE_SEGMENT, stream=None):
+    _check(lib().up_block_offsets(batch.ref, block_size, _p(score_flags), int(score_scope),
+                                  _p(cu_blocks), _stream(stream)), "up_block_offsets")
 
 
-def up_attn_workspace_bytes(batch: Batch, dtype, Hq, Hkv, D, block_size=0) -> int:
+def up_attn_workspace_bytes(batch: Batch, dtype, Hq, Hkv, D, block_size=0,
+                            score_scope=UP_SCOPE_SEGMENT) -> int:
     """``block_size``: the scoring block size when scores are asked for, else 0."""
-    return int(lib().up_attn_workspace_bytes(batch.ref, _DT[dtype], Hq, Hkv, D, int(block_size)))
+    return int(lib().up_attn_workspace_bytes(batch.ref, _DT[dtype], Hq, Hkv, D, int(block_size),
+                                             int(score_scope)))
 
 
 def up_prefill_attn(batch: Batch, q, k, v, k_cache, v_cache, out, workspace, *, rope_theta=0.0,
-                    window=0, sm_scale=0.0, score_flags=None, block_size=0, cu_blocks=None,
-                    block_mass=None, lse=None, stream=None):
+                    window=0, sm_scale=0.0, score_flags=None, block_size=0,
+                    score_scope=UP_SCOPE_SEGMENT, cu_blocks=None, block_mass=None, lse=None,
+                    stream=None):
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, k_cache, v_cache, out)):
         raise UniprefillError("q, k, v, caches and out must share one dtype (float32 or bfloat16)")
     _check(lib().up_prefill_attn(batch.ref, _DT[q.dtype], Hq, Hkv, D, _p(q), _p(k), _p(v),
                                  _p(k_cache), _p(v_cache), float(rope_theta), int(window),
-                                 float(sm_scale), _p(score_flags), int(block_size), _p(cu_blocks),
+                                 float(sm_scale), _p(score_flags), int(block_size),
+                                 int(score_scope), _p(cu_blocks),
                                  _p(block_mass), _p(out), _p(lse), _p(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "up_prefill_attn")
@@ -187,14 +195,15 @@ def up_compact_workspace_bytes(num_seqs, num_blocks) -> int:
 
 
 def up_compact(batch: Batch, block_size, cu_blocks, keep, num_blocks, rows, index_map,
-               cu_seqlens_out, num_kept, workspace, stream=None):
+               cu_seqlens_out, num_kept, workspace, score_flags=None,
+               score_scope=UP_SCOPE_SEGMENT, stream=None):
     """``rows``: list of (src, dst) tensors whose first dimension is the token."""
     arr = (UpRows * max(1, len(rows)))()
     for i, (src, dst) in enumerate(rows):
         rb = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
         arr[i] = UpRows(_p(src).value, _p(dst).value, rb)
-    _check(lib().up_compact(batch.ref, block_size, _p(cu_blocks), _p(keep), int(num_blocks),
-                            len(rows), arr, _p(index_map), _p(cu_seqlens_out), _p(num_kept),
+    _check(lib().up_compact(batch.ref, block_size, _p(cu_blocks), _p(score_flags),
+                            int(score_scope), _p(keep), int(num_blocks), len(rows), arr, _p(index_map), _p(cu_seqlens_out), _p(num_kept),
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)), "up_compact")
 
@@ -285,3 +294,14 @@ def up_linear_attn_bf16(cu_seqlens, q, k, v, out, stream=None):
                                      ctypes.c_void_p(k.data_ptr()), k.stride(0),
                                      ctypes.c_void_p(v.data_ptr()), v.stride(0), Hq, Hkv, D,
                                      _p(out), _stream(stream)), "up_linear_attn_bf16")
+
+
+def up_kept_cache_slots(batch: Batch, block_size, cu_blocks, score_flags, keep, num_blocks, slots,
+                        cu_slots_out, num_slots, workspace, stream=None):
+    """KV slots of the kept cached tokens under whole-prompt scoring
+    (``slots``: int32 tensor whose length is the capacity)."""
+    _check(lib().up_kept_cache_slots(batch.ref, block_size, _p(cu_blocks), _p(score_flags),
+                                     _p(keep), int(num_blocks), _p(slots), slots.numel(),
+                                     _p(cu_slots_out), _p(num_slots), _p(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)), "up_kept_cache_slots")

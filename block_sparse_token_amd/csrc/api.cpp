@@ -52,6 +52,25 @@ up_status check_batch(const up_batch* b, bool need_positions) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// whole-prompt scoring reads the cached lengths, and its workspace bound
+// uses the block table's width (cached tokens <= max_pages * page_size)
+up_status check_scope(const up_batch* b, int32_t scope) {
+  if (scope != UP_SCOPE_SEGMENT && scope != UP_SCOPE_PROMPT)
+    return fail(UP_ERR_INVALID, "score_scope must be UP_SCOPE_SEGMENT or UP_SCOPE_PROMPT (got %d)",
+                scope);
+  if (scope == UP_SCOPE_PROMPT && (!b->ctx_lens || !b->block_table || b->max_pages <= 0))
+    return fail(UP_ERR_INVALID, "whole-prompt scoring needs ctx_lens and a block table");
+  return UP_OK;
+}
+
+up::BlockOrigin block_origin(const up_batch* b, const uint8_t* flags, int32_t scope) {
+  up::BlockOrigin bo;
+  bo.ctx_lens = b->ctx_lens;
+  bo.flags = flags;
+  bo.prompt_scope = scope == UP_SCOPE_PROMPT && flags;
+  return bo;
+}
+
 // UP_DEBUG_CHECKS=1 in the environment: up_prefill_attn checks the batch's
 // device-side preconditions first (and synchronises on the result).
 bool debug_checks() {
@@ -179,15 +198,19 @@ up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap
                        "linear launch");
 }
 
-up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
-                           void* stream) {
+up_status up_block_offsets(const up_batch* batch, int32_t block_size, const uint8_t* score_flags,
+                           int32_t score_scope, int32_t* cu_blocks, void* stream) {
   up_status st = check_batch(batch, false);
+  if (st) return st;
+  st = check_scope(batch, score_scope);
   if (st) return st;
   if (!valid_block_size(block_size))
     return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
   if (!cu_blocks) return fail(UP_ERR_INVALID, "cu_blocks is NULL");
-  return device_status(up::launch_block_offsets(batch->cu_seqlens, batch->num_seqs, block_size,
-                                                cu_blocks, as_stream(stream)),
+  return device_status(up::launch_block_offsets(batch->cu_seqlens,
+                                                block_origin(batch, score_flags, score_scope),
+                                                batch->num_seqs, block_size, cu_blocks,
+                                                as_stream(stream)),
                        "block offsets launch");
 }
 
@@ -195,15 +218,18 @@ namespace {
 // bf16 scoring scratch: runs of min(block, 64) keys of every block, one
 // value per last-block row and head, plus one total per last-block row and
 // head of every segment
-size_t score_runs(const up_batch* b, int block_size) {
-  const size_t nb_cap = (size_t)(b->num_tokens + block_size - 1) / block_size + b->num_seqs;
+size_t score_runs(const up_batch* b, int block_size, int scope) {
+  const size_t cached =
+      scope == UP_SCOPE_PROMPT ? (size_t)b->num_seqs * b->max_pages * up::kPageSize : 0;
+  const size_t nb_cap =
+      ((size_t)b->num_tokens + cached + block_size - 1) / block_size + b->num_seqs;
   return nb_cap * (size_t)(block_size / (block_size < 64 ? block_size : 64));
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
-                               int32_t D, int32_t block_size) {
+                               int32_t D, int32_t block_size, int32_t score_scope) {
   if (!batch || Hkv <= 0 || Hq <= 0 || Hq % Hkv) return 0;
   const int G = Hq / Hkv;
   if (G > 32) return 0;
@@ -213,7 +239,7 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
   if (dtype == UP_BF16 && block_size != 0) {
     if (!valid_block_size(block_size)) return 0;
     bytes = align256(bytes);
-    bytes += sizeof(float) * score_runs(batch, block_size) * block_size * Hq;
+    bytes += sizeof(float) * score_runs(batch, block_size, score_scope) * block_size * Hq;
     bytes += sizeof(float) * (size_t)batch->num_seqs * block_size * Hq;
   }
   return bytes;
@@ -222,11 +248,15 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
 up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
                           int32_t D, const void* q, const void* k, const void* v, void* k_cache,
                           void* v_cache, float rope_theta, int32_t window, float sm_scale,
-                          const uint8_t* score_flags, int32_t block_size,
+                          const uint8_t* score_flags, int32_t block_size, int32_t score_scope,
                           const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream) {
   up_status st = check_batch(batch, true);
   if (st) return st;
+  st = check_scope(batch, score_scope);
+  if (st) return st;
+  if (score_scope == UP_SCOPE_PROMPT && dtype != UP_BF16)
+    return fail(UP_ERR_UNSUPPORTED, "whole-prompt scoring is built for the bf16 path only");
   if (dtype != UP_F32 && dtype != UP_BF16) return fail(UP_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
     return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
@@ -251,7 +281,7 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
     return fail(UP_ERR_UNSUPPORTED, "at most %d segments per call (got %d)", up::kMaxSeqsPlan,
                 batch->num_seqs);
   const size_t need =
-      up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D, score_flags ? block_size : 0);
+      up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D, score_flags ? block_size : 0, score_scope);
   if (workspace_bytes < need)
     return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
 
@@ -312,7 +342,7 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   a.score_lse = nullptr;
   if (bf16 && score_flags) {
     a.score_part = (float*)((char*)workspace + align256(16 + sizeof(int2) * (size_t)cap));
-    a.score_lse = a.score_part + score_runs(batch, block_size) * block_size * Hq;
+    a.score_lse = a.score_part + score_runs(batch, block_size, score_scope) * block_size * Hq;
   }
   a.items = items;
   a.item_count = count;
@@ -321,6 +351,7 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   a.G = G;
   a.max_pages = batch->max_pages;
   a.block_size = block_size;
+  a.score_scope = score_flags && score_scope == UP_SCOPE_PROMPT;
   a.window = window > 0 ? window : 0;
   a.rope = rope;
   a.scale = sm_scale > 0.f ? sm_scale : (float)(1.0 / sqrt((double)D));
@@ -383,10 +414,13 @@ size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks) {
 }
 
 up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
-                     const uint8_t* keep, int32_t num_blocks, int32_t n_rows,
-                     const up_rows* rows, int32_t* index_map, int32_t* cu_seqlens_out,
-                     int32_t* num_kept, void* workspace, size_t workspace_bytes, void* stream) {
+                     const uint8_t* score_flags, int32_t score_scope, const uint8_t* keep,
+                     int32_t num_blocks, int32_t n_rows, const up_rows* rows,
+                     int32_t* index_map, int32_t* cu_seqlens_out, int32_t* num_kept,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   up_status st = check_batch(batch, false);
+  if (st) return st;
+  st = check_scope(batch, score_scope);
   if (st) return st;
   if (!valid_block_size(block_size))
     return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
@@ -411,7 +445,9 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
     return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   int32_t* block_out = (int32_t*)workspace;
   int32_t* block_seg = block_out + num_blocks + 4;
-  return device_status(up::launch_compact(batch->cu_seqlens, cu_blocks, keep, batch->num_seqs,
+  return device_status(up::launch_compact(batch->cu_seqlens, cu_blocks,
+                                          block_origin(batch, score_flags, score_scope), keep,
+                                          batch->num_seqs,
                                           num_blocks, block_size, rc, n_rows, index_map,
                                           cu_seqlens_out, num_kept, block_out, block_seg,
                                           as_stream(stream)),
@@ -419,3 +455,35 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
 }
 
 }  // extern "C"
+
+up_status up_kept_cache_slots(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                              const uint8_t* score_flags, const uint8_t* keep, int32_t num_blocks,
+                              int32_t* slots, int32_t slots_cap, int32_t* cu_slots_out,
+                              int32_t* num_slots, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  st = check_scope(batch, UP_SCOPE_PROMPT);
+  if (st) return st;
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+  if (!cu_blocks || !score_flags || !keep || !slots || !cu_slots_out || !num_slots)
+    return fail(UP_ERR_INVALID,
+                "cu_blocks, score_flags, keep, slots, cu_slots_out and num_slots must be non-NULL");
+  if (num_blocks < batch->num_seqs)
+    return fail(UP_ERR_INVALID, "num_blocks (%d) < num_seqs (%d)", num_blocks, batch->num_seqs);
+  if (slots_cap < 0) return fail(UP_ERR_INVALID, "slots_cap must be >= 0 (got %d)", slots_cap);
+  if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
+  const size_t need = up_compact_workspace_bytes(batch->num_seqs, num_blocks);
+  if (workspace_bytes < need)
+    return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  int32_t* block_out = (int32_t*)workspace;
+  int32_t* block_seg = block_out + num_blocks + 4;
+  return device_status(
+      up::launch_kept_cache_slots(batch->cu_seqlens, cu_blocks, keep,
+                                  block_origin(batch, score_flags, UP_SCOPE_PROMPT),
+                                  batch->block_table, batch->max_pages, batch->num_seqs,
+                                  num_blocks, block_size, slots, slots_cap, cu_slots_out,
+                                  num_slots, block_out, block_seg, as_stream(stream)),
+      "kept cache slots launch");
+}

@@ -483,6 +483,9 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const bool row_scores = item_scores && rvalid && i >= r0s && h == 0;
   const int Qs = scored ? min(Bs, C::BN) : C::BN;
   const int run_base = scored ? a.cu_blocks[s] * (Bs / Qs) : 0;
+  // first key of the scored blocks: the segment's first own key, or key 0
+  // when the whole prompt is scored (cached length a multiple of the block)
+  const int c0 = (scored && a.score_scope) ? 0 : sg.c;
   float* run_lse = row_scores ? a.score_part + (long)(i - r0s) * a.Hq + g * G + hh : nullptr;
   const long run_stride = (long)Bs * a.Hq;  // between consecutive runs
   const Stager<C> st{a,   sg,  g, t0, u_end, __builtin_amdgcn_readfirstlane(w),
@@ -556,12 +559,11 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[db], 0, 0, 0);
       }
     }
-    // scored segment, last block's rows, own-key tile: the log2-sum-exp of
-    // each run of Qs own keys (after the products, so the branch does not
-    // split the softmax and PV work)
+    // scored segment, last block's rows, tile with scored keys: the
+    // log2-sum-exp of each run of Qs keys from c0 (after the products, so
+    // the branch does not split the softmax and PV work)
     const int u0 = t0 + t * C::BN;
-    if (SC && item_scores && u0 >= sg.c) {
-      const int own0 = u0 - sg.c;
+    if (SC && item_scores && u0 + C::BN > c0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int q = Qs == 16 ? j : Qs == 32 ? (j >> 1) : 0;
@@ -569,8 +571,9 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
         if (!head) continue;
         const float part = Qs == 16 ? rk[j] : Qs == 32 ? rk[j] + rk[j + 1] : rs;
         const float x = pair_sum(part);
-        if (row_scores && own0 + q * Qs < sg.n)
-          run_lse[(long)(run_base + own0 / Qs + q) * run_stride] = ms + __log2f(x);
+        const int ustart = u0 + q * Qs;
+        if (row_scores && ustart >= c0 && ustart < sg.c + sg.n)
+          run_lse[(long)(run_base + (ustart - c0) / Qs) * run_stride] = ms + __log2f(x);
       }
     }
     return rs;
@@ -661,7 +664,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   if (row_scores) {
     a.score_lse[((long)s * Bs + (i - r0s)) * a.Hq + g * G + hh] = ms + __log2f(ltot);
     // runs before the first tile (outside the window of every row here)
-    for (int q = 0; q < (t0 - sg.c) / Qs; ++q)
+    for (int q = 0; q < (t0 - c0) / Qs; ++q)
       run_lse[(long)(run_base + q) * run_stride] = -INFINITY;
   }
   if (!rvalid) return;

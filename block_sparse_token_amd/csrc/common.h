@@ -26,6 +26,20 @@ inline size_t work_capacity(int T, int S, int positions_per_tile) {
 }
 
 // ---------------------------------------------------------------- kernel parameters
+// Where a segment's blocks start: at its own first token, or, for a scored
+// segment under whole-prompt scoring, at its prompt's first token (the
+// cached tokens form the first blocks; their count is a multiple of the
+// block size).  ``of(s)`` is the number of the segment's tokens before its
+// own first one that its blocks cover.
+struct BlockOrigin {
+  const int32_t* ctx_lens;
+  const uint8_t* flags;
+  int prompt_scope;
+  __device__ inline int of(int s) const {
+    return (prompt_scope && flags && flags[s]) ? ctx_lens[s] : 0;
+  }
+};
+
 struct AttnArgs {
   const void* q;
   void* out;
@@ -47,6 +61,7 @@ struct AttnArgs {
   const int2* items;
   const int32_t* item_count;
   int Hq, Hkv, G, max_pages, block_size, window, rope;
+  int score_scope;   // 1: scored segments are scored over their whole prompt
   float scale;       // logit scale (1/sqrt(D) by default)
   float scale_log2;  // scale * log2(e)
   // rotary frequencies: rev[j] = theta^(-2j/D) / (2 pi) (turns per position)
@@ -88,7 +103,7 @@ hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void*
                                    int Hq, int Hkv, void* out, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int rows_cap,
                               const int32_t* rows_dev, int N, int K, int act, hipStream_t st);
-hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,
+hipError_t launch_block_offsets(const int32_t* cu_seqlens, const BlockOrigin& bo, int S, int block_size,
                                 int32_t* cu_blocks, hipStream_t st);
 hipError_t launch_plan(const int32_t* cu_seqlens, const int32_t* ctx_lens,
                        const uint8_t* score_flags, int S, int positions_per_tile, int window,
@@ -110,7 +125,13 @@ struct RowCopy {
   int64_t row_bytes;
 };
 constexpr int kMaxRowTensors = 16;
-hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+hipError_t launch_kept_cache_slots(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                   const uint8_t* keep, const BlockOrigin& bo,
+                                   const int32_t* block_table, int max_pages, int S,
+                                   int num_blocks, int block_size, int32_t* slots, int slots_cap,
+                                   int32_t* cu_out, int32_t* num_out, int32_t* block_out,
+                                   int32_t* block_seg, hipStream_t st);
+hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks, const BlockOrigin& bo,
                           const uint8_t* keep, int S, int num_blocks, int block_size,
                           const RowCopy* rows, int n_rows, int32_t* index_map,
                           int32_t* cu_seqlens_out, int32_t* num_kept, int32_t* block_out,

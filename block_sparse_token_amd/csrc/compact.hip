@@ -2,6 +2,10 @@
 // the removed tokens take no part in any later sublayer, so later layers see
 // only the kept rows).
 //
+// Under whole-prompt scoring a scored segment's first blocks are its cached
+// tokens (BlockOrigin): they hold none of the call's rows, and a second
+// entry lists the KV slots of the kept ones instead.
+//
 // Pass 1 (one workgroup): exclusive scan over blocks of (kept ? length : 0)
 // gives each kept block's first output row, the per-segment output offsets
 // (cu_seqlens_out) and the kept count.  Pass 2: the rows of one block are
@@ -12,9 +16,12 @@
 
 namespace up {
 
+// cached = false: each block counts its kept own rows; cached = true: each
+// kept block of cached tokens counts its B tokens.
 __global__ __launch_bounds__(1024) void compact_scan_kernel(
     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ cu_blocks,
-    const uint8_t* __restrict__ keep, int S, int B, int32_t* __restrict__ block_out,
+    const uint8_t* __restrict__ keep, BlockOrigin bo, bool cached, int S, int B,
+    int32_t* __restrict__ block_out,
     int32_t* __restrict__ block_seg, int32_t* __restrict__ cu_out, int32_t* __restrict__ num_kept) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
@@ -33,8 +40,9 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(
       }
       s = lo;
       const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-      const int i0 = (k - cu_blocks[s]) * B;
-      v = keep[k] ? min(B, n - i0) : 0;
+      const int i0 = (k - cu_blocks[s]) * B - bo.of(s);  // first own row of the block
+      if (cached) v = keep[k] && i0 < 0 ? B : 0;
+      else v = keep[k] && i0 >= 0 ? min(B, n - i0) : 0;
       block_seg[k] = s;
     }
     int x = v;
@@ -65,6 +73,7 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(
 struct GatherArgs {
   const int32_t* cu_seqlens;
   const int32_t* cu_blocks;
+  BlockOrigin bo;
   const uint8_t* keep;
   const int32_t* block_out;
   const int32_t* block_seg;
@@ -112,7 +121,8 @@ __global__ __launch_bounds__(256) void compact_gather_kernel(GatherArgs g) {
   if (k >= NB || !g.keep[k]) return;
   const int s = g.block_seg[k];
   const int n = g.cu_seqlens[s + 1] - g.cu_seqlens[s];
-  const int i0 = (k - g.cu_blocks[s]) * g.B;
+  const int i0 = (k - g.cu_blocks[s]) * g.B - g.bo.of(s);
+  if (i0 < 0) return;  // a block of cached tokens: no rows in this call
   const int len = min(g.B, n - i0);
   const int src_row = g.cu_seqlens[s] + i0;
   const int dst_row = g.block_out[k];
@@ -126,18 +136,55 @@ __global__ __launch_bounds__(256) void compact_gather_kernel(GatherArgs g) {
   }
 }
 
-hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+// Kept cached tokens of whole-prompt-scored segments: token u of block k
+// goes to slots[block_out[k] + u - first token of k] as its KV slot
+// block_table[s][u / 16] * 16 + u % 16 (never past slots_cap).
+__global__ __launch_bounds__(256) void kept_cache_slots_kernel(
+    const int32_t* __restrict__ cu_blocks, const uint8_t* __restrict__ keep, BlockOrigin bo,
+    const int32_t* __restrict__ block_table, int max_pages, int S, int B,
+    const int32_t* __restrict__ block_out, const int32_t* __restrict__ block_seg,
+    int32_t* __restrict__ slots, int slots_cap) {
+  const int k = blockIdx.x;
+  if (k >= cu_blocks[S] || !keep[k]) return;
+  const int s = block_seg[k];
+  const int u0 = (k - cu_blocks[s]) * B;
+  if (u0 >= bo.of(s)) return;  // a block of the segment's own rows
+  for (int r = threadIdx.x; r < B; r += 256) {
+    const int u = u0 + r, d = block_out[k] + r;
+    if (d < slots_cap)
+      slots[d] = block_table[(long)s * max_pages + (u >> 4)] * kPageSize + (u & (kPageSize - 1));
+  }
+}
+
+hipError_t launch_kept_cache_slots(const int32_t* cu_seqlens, const int32_t* cu_blocks,
+                                   const uint8_t* keep, const BlockOrigin& bo,
+                                   const int32_t* block_table, int max_pages, int S,
+                                   int num_blocks, int block_size, int32_t* slots, int slots_cap,
+                                   int32_t* cu_out, int32_t* num_out, int32_t* block_out,
+                                   int32_t* block_seg, hipStream_t st) {
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, cu_blocks, keep,
+                     bo, true, S, block_size, block_out, block_seg, cu_out, num_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kept_cache_slots_kernel, dim3(num_blocks), dim3(256), 0, st, cu_blocks, keep,
+                     bo, block_table, max_pages, S, block_size, block_out, block_seg, slots,
+                     slots_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks, const BlockOrigin& bo,
                           const uint8_t* keep, int S, int num_blocks, int block_size,
                           const RowCopy* rows, int n_rows, int32_t* index_map,
                           int32_t* cu_seqlens_out, int32_t* num_kept, int32_t* block_out,
                           int32_t* block_seg, hipStream_t st) {
   hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, cu_blocks, keep,
-                     S, block_size, block_out, block_seg, cu_seqlens_out, num_kept);
+                     bo, false, S, block_size, block_out, block_seg, cu_seqlens_out, num_kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   GatherArgs g;
   g.cu_seqlens = cu_seqlens;
   g.cu_blocks = cu_blocks;
+  g.bo = bo;
   g.keep = keep;
   g.block_out = block_out;
   g.block_seg = block_seg;

@@ -21,6 +21,8 @@ constexpr int kMassGroups = 32;
 __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restrict__ cu_seqlens,
                                                          const uint8_t* __restrict__ score_flags,
                                                          const int32_t* __restrict__ cu_blocks,
+                                                         const int32_t* __restrict__ ctx_lens,
+                                                         int prompt_scope,
                                                          const float* __restrict__ score_part,
                                                          const float* __restrict__ score_lse,
                                                          int Hq, int B, float* __restrict__ mass) {
@@ -29,9 +31,13 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restri
   const int s = blockIdx.x;
   if (!score_flags[s]) return;
   const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-  const int nb = (n + B - 1) / B;
+  // whole-prompt scoring: blocks from the prompt's first token; off = the
+  // cached tokens they cover (a multiple of B, so the last block is the
+  // segment's own last block either way)
+  const int off = prompt_scope ? ctx_lens[s] : 0;
+  const int nb = (off + n + B - 1) / B;
   if ((int)blockIdx.y >= nb) return;
-  const int r0 = (nb - 1) * B, rows = n - r0;
+  const int r0 = ((n + B - 1) / B - 1) * B, rows = n - r0;
   const int Q = min(B, 64), rpb = B / Q;
   const long run_base = (long)cu_blocks[s] * rpb;
   const int tid = threadIdx.x, rg = tid >> 5, hl = tid & 31;
@@ -49,7 +55,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restri
 #pragma unroll 4
         for (int rl = rg; rl < rows; rl += 8) {
           const float t = tot[rl * 32 + hl];
-          for (int j = 0; j < rpb && b * B + j * Q <= r0 + rl; ++j)
+          for (int j = 0; j < rpb && b * B + j * Q <= off + r0 + rl; ++j)
             acc += exp2f(score_part[((run_base + b * rpb + j) * B + rl) * Hq + h] - t);
         }
       }
@@ -68,8 +74,8 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restri
 
 hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st) {
   hipLaunchKernelGGL(block_mass_kernel, dim3(S, kMassGroups), dim3(256), 0, st, a.cu_seqlens,
-                     a.score_flags, a.cu_blocks, a.score_part, a.score_lse, a.Hq, a.block_size,
-                     a.block_mass);
+                     a.score_flags, a.cu_blocks, a.ctx_lens, a.score_scope, a.score_part,
+                     a.score_lse, a.Hq, a.block_size, a.block_mass);
   return hipGetLastError();
 }
 

@@ -6,9 +6,10 @@
 
 namespace up {
 
-// cu_blocks[s+1] = cu_blocks[s] + ceil(n_s / B); one workgroup, chunked scan.
+// cu_blocks[s+1] = cu_blocks[s] + ceil((origin_s + n_s) / B); one workgroup,
+// chunked scan.
 __global__ __launch_bounds__(1024) void block_offsets_kernel(const int32_t* __restrict__ cu_seqlens,
-                                                             int S, int B,
+                                                             BlockOrigin bo, int S, int B,
                                                              int32_t* __restrict__ cu_blocks) {
   __shared__ int32_t wsum[16];
   __shared__ int32_t carry;
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(1024) void block_offsets_kernel(const int32_t* __re
   for (int base = 0; base < S; base += 1024) {
     const int s = base + tid;
     int v = 0;
-    if (s < S) v = (cu_seqlens[s + 1] - cu_seqlens[s] + B - 1) / B;
+    if (s < S) v = (cu_seqlens[s + 1] - cu_seqlens[s] + bo.of(s) + B - 1) / B;
     // inclusive wave scan
     int x = v;
 #pragma unroll
@@ -40,10 +41,10 @@ __global__ __launch_bounds__(1024) void block_offsets_kernel(const int32_t* __re
   }
 }
 
-hipError_t launch_block_offsets(const int32_t* cu_seqlens, int S, int block_size,
-                                int32_t* cu_blocks, hipStream_t st) {
-  hipLaunchKernelGGL(block_offsets_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, S, block_size,
-                     cu_blocks);
+hipError_t launch_block_offsets(const int32_t* cu_seqlens, const BlockOrigin& bo, int S,
+                                int block_size, int32_t* cu_blocks, hipStream_t st) {
+  hipLaunchKernelGGL(block_offsets_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, bo, S,
+                     block_size, cu_blocks);
   return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ class PrefillCall:
     rows: list = field(default_factory=list)  # [(name, src tensor)] to compact
     with_lse: bool = False
     compact: bool = True
+    score_scope: int = B.UP_SCOPE_SEGMENT  # UP_SCOPE_PROMPT: whole-prompt scoring
 
     def __post_init__(self):
         dev = self.q.device
@@ -76,7 +77,7 @@ class PrefillCall:
         scoring = self.flags is not None
         self.block_mass = torch.empty(NB * Hq, dtype=torch.float32, device=dev) if scoring else None
         nbytes = B.up_attn_workspace_bytes(self.batch, self.q.dtype, Hq, self.k.shape[1], D,
-                                           self.block_size if scoring else 0)
+                                           self.block_size if scoring else 0, self.score_scope)
         self.attn_ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.scores = torch.empty(NB, dtype=torch.float32, device=dev)
         self.keep = torch.empty(NB, dtype=torch.uint8, device=dev)
@@ -91,10 +92,11 @@ class PrefillCall:
     # individual stages (each one library call, or two for scoring)
     def attention(self, stream=None):
         B.up_block_offsets(self.batch, self.block_size if self.block_size else 16, self.cu_blocks,
-                           stream)
+                           score_flags=self.flags, score_scope=self.score_scope, stream=stream)
         B.up_prefill_attn(self.batch, self.q, self.k, self.v, self.k_cache, self.v_cache, self.out,
                           self.attn_ws, rope_theta=self.rope_theta, window=self.window,
                           score_flags=self.flags, block_size=self.block_size,
+                          score_scope=self.score_scope,
                           cu_blocks=self.cu_blocks if self.flags is not None else None,
                           block_mass=self.block_mass, lse=self.lse, stream=stream)
 
@@ -109,7 +111,8 @@ class PrefillCall:
     def compact_stage(self, stream=None):
         rows = [(src, self.rows_out[name]) for name, src in self.rows]
         B.up_compact(self.batch, self.block_size, self.cu_blocks, self.keep, self.num_blocks, rows,
-                     self.index_map, self.cu_seqlens_out, self.num_kept, self.compact_ws, stream)
+                     self.index_map, self.cu_seqlens_out, self.num_kept, self.compact_ws,
+                     score_flags=self.flags, score_scope=self.score_scope, stream=stream)
 
     def launch(self, stream=None):
         self.attention(stream)

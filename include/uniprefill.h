@@ -95,23 +95,44 @@ typedef struct up_batch {
 } up_batch;
 
 /*
- * Block offsets: cu_blocks[s+1] - cu_blocks[s] = ceil(n_s / block_size),
- * cu_blocks[0] = 0, blocks counted from each segment's start (the last one
- * may be short).  cu_blocks: [S+1] int32 output.
- * block_size: 16, 32, 64 or 128.
+ * Scoring scope (score_scope arguments below).
+ *  UP_SCOPE_SEGMENT: a scored segment's blocks are its own tokens, counted
+ *    from its first one; cached keys enter the softmax normaliser only.
+ *  UP_SCOPE_PROMPT: whole-prompt scoring for the final chunk of a chunked
+ *    prompt (review, Method & Key Results: importance per block of the
+ *    input; glossary, How chunked prefill works: a chunk sees the cached
+ *    keys of the earlier chunks): a scored segment's blocks are those of its
+ *    whole prompt, the ctx_len cached tokens first, so cached blocks are
+ *    scored and selected too.  Needs ctx_lens and a block table; device
+ *    precondition: ctx_lens[s] of every scored segment a multiple of
+ *    block_size (so the prompt's last block is the segment's last block).
+ *    Unscored segments keep their own blocks.  Built for UP_BF16.
  */
-up_status up_block_offsets(const up_batch* batch, int32_t block_size, int32_t* cu_blocks,
-                           void* stream);
+#define UP_SCOPE_SEGMENT 0
+#define UP_SCOPE_PROMPT 1
+
+/*
+ * Block offsets: cu_blocks[s+1] - cu_blocks[s] = ceil((o_s + n_s) /
+ * block_size), cu_blocks[0] = 0, where o_s = ctx_lens[s] for a scored
+ * segment (score_flags[s] != 0) under UP_SCOPE_PROMPT and 0 otherwise;
+ * blocks are counted from that start (the last one may be short).
+ * cu_blocks: [S+1] int32 output.  block_size: 16, 32, 64 or 128.
+ * score_flags may be NULL (no segment scored).
+ */
+up_status up_block_offsets(const up_batch* batch, int32_t block_size, const uint8_t* score_flags,
+                           int32_t score_scope, int32_t* cu_blocks, void* stream);
 
 /*
  * Workspace bytes up_prefill_attn needs for this batch shape: the work list
  * of query tiles (and, for UP_F32, score items), plus for UP_BF16 with
  * scoring the per-row run sums of the segments' last blocks.  block_size:
  * the block size up_prefill_attn will be called with when it gets
- * score_flags, else 0.  Returns 0 for an unsupported shape.
+ * score_flags, else 0; score_scope as it will be called with (the bound for
+ * UP_SCOPE_PROMPT counts max_pages * page_size cached tokens per segment).
+ * Returns 0 for an unsupported shape.
  */
 size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
-                               int32_t D, int32_t block_size);
+                               int32_t D, int32_t block_size, int32_t score_scope);
 
 /*
  * Attention with rotary positions, KV-cache write and fused block mass.
@@ -135,8 +156,10 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
  *     sum over rows t of the segment's last block (local rows
  *     [(nb-1)*block_size, n)) of the softmax probability that row t, head h,
  *     puts on the segment's own keys of block b
- * (cached keys enter the softmax normaliser but are not scored).  Entries of
- * unflagged segments are not written.
+ * (cached keys enter the softmax normaliser but are not scored).  Under
+ * UP_SCOPE_PROMPT the blocks b are those of the whole prompt (cached keys
+ * included, see UP_SCOPE_PROMPT) and the rows those of its last block.
+ * Entries of unflagged segments are not written.
  *
  * dtype: UP_F32 (q, k, v, caches, out float32) or UP_BF16 (all bf16;
  *        products on bf16 matrix cores, softmax and accumulation in fp32).
@@ -147,7 +170,8 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
  * k_cache, v_cache [num_pages, Hkv, page_size, D], read and written.
  * sm_scale: logit scale; <= 0 selects 1/sqrt(D).
  * score_flags [S] u8, may be NULL (no scoring); then cu_blocks and
- *        block_mass may be NULL.  block_size as in up_block_offsets.
+ *        block_mass may be NULL.  block_size and score_scope as in
+ *        up_block_offsets (UP_SCOPE_PROMPT with UP_F32: UP_ERR_UNSUPPORTED).
  * block_mass [NB, Hq] f32 (NB = cu_blocks[S]).
  * out [T, Hq, D] (dtype); lse [T, Hq] f32 natural-log normaliser of each
  *        row's scaled logits, or NULL.
@@ -156,7 +180,7 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
 up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
                           int32_t D, const void* q, const void* k, const void* v, void* k_cache,
                           void* v_cache, float rope_theta, int32_t window, float sm_scale,
-                          const uint8_t* score_flags, int32_t block_size,
+                          const uint8_t* score_flags, int32_t block_size, int32_t score_scope,
                           const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
@@ -201,7 +225,10 @@ size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks);
  * Compaction of the kept tokens (review, Method & Key Results: dropped
  * tokens are removed from all later sublayers).  Token t of segment s is
  * kept when its block (local index / block_size) has keep[cu_blocks[s] + b]
- * != 0.  Outputs, in ascending original order:
+ * != 0; under UP_SCOPE_PROMPT a scored segment's own token i is in block
+ * (ctx_lens[s] + i) / block_size of its prompt (score_flags and
+ * score_scope as given to up_block_offsets; score_flags may be NULL with
+ * UP_SCOPE_SEGMENT).  Outputs, in ascending original order:
  *   index_map [T cap] i32: packed index of each kept token;
  *   cu_seqlens_out [S+1] i32: per-segment kept counts, prefix-summed;
  *   num_kept [1] i32 (device);
@@ -211,10 +238,31 @@ size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks);
  * workspace: at least up_compact_workspace_bytes(S, num_blocks) bytes.
  */
 up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
-                     const uint8_t* keep, int32_t num_blocks, int32_t n_rows,
-                     const up_rows* rows /* (host) array of n_rows */, int32_t* index_map,
-                     int32_t* cu_seqlens_out, int32_t* num_kept, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     const uint8_t* score_flags, int32_t score_scope, const uint8_t* keep,
+                     int32_t num_blocks, int32_t n_rows, const up_rows* rows /* (host) array of n_rows */,
+                     int32_t* index_map, int32_t* cu_seqlens_out, int32_t* num_kept,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Whole-prompt scoring (UP_SCOPE_PROMPT): the KV slots of the kept cached
+ * tokens of every scored segment, for the later layers' attention over the
+ * kept context (review, Method & Key Results: dropped tokens take no part
+ * in later sublayers).  Cached token u (position u) of scored segment s is
+ * kept when block u / block_size of its prompt is; its slot is
+ * block_table[s * max_pages + u / page_size] * page_size + u % page_size.
+ * Outputs, segment by segment, positions ascending:
+ *   slots [slots_cap] i32 (entries past slots_cap are not written; a cap of
+ *   num_seqs * max_pages * page_size always suffices);
+ *   cu_slots_out [S+1] i32: per-segment counts, prefix-summed;
+ *   num_slots [1] i32 (device): the total.
+ * cu_blocks, score_flags and keep as given to up_compact under
+ * UP_SCOPE_PROMPT; workspace as for up_compact.
+ */
+up_status up_kept_cache_slots(const up_batch* batch, int32_t block_size, const int32_t* cu_blocks,
+                              const uint8_t* score_flags, const uint8_t* keep, int32_t num_blocks,
+                              int32_t* slots, int32_t slots_cap, int32_t* cu_slots_out,
+                              int32_t* num_slots, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Later-layer linear map on the kept tokens (UniPrefill review, Method & Key

@@ -33,8 +33,9 @@ def initial_cache(wl) -> KVCacheModel:
     return cache
 
 
-def run_workload(wl, threads=None, cache=None, layer2=True):
-    """Oracle results for every call of ``wl`` (a list of dicts)."""
+def run_workload(wl, threads=None, cache=None, layer2=True, scope="segment"):
+    """Oracle results for every call of ``wl`` (a list of dicts); ``scope``
+    "prompt" scores the flagged segments over their whole prompt."""
     cache = cache if cache is not None else initial_cache(wl)
     results = []
     for call in wl.calls:
@@ -42,7 +43,7 @@ def run_workload(wl, threads=None, cache=None, layer2=True):
                        k=to_f64(call.k, wl.dtype), v=to_f64(call.v, wl.dtype),
                        positions=call.positions, cu_seqlens=call.cu_seqlens, Hq=wl.Hq, Hkv=wl.Hkv,
                        D=wl.D, theta=wl.theta, window=wl.window, block_size=wl.block_size, p=wl.p,
-                       cache=cache, rows=row_tensors(call), threads=threads)
+                       cache=cache, rows=row_tensors(call), threads=threads, scope=scope)
         if layer2 and wl.layer2 is not None:
             res["layer2"] = run_layer2(wl, call, res, threads=threads)
         results.append(res)

@@ -21,6 +21,7 @@ import torch
 import oracle
 import workloads as W
 from workloads import device as WD
+from block_sparse_token_amd import binding as B
 from block_sparse_token_amd import step as ST
 
 F32_REL = 1e-5
@@ -54,16 +55,19 @@ def row_sources(call, device="cuda"):
     return WD.row_sources(call, device)
 
 
-def launch_call(wl, call, kc, vc, *, with_lse=True, compact=True, device="cuda", flags=True):
+def launch_call(wl, call, kc, vc, *, with_lse=True, compact=True, device="cuda", flags=True,
+                whole_prompt=False):
     batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
                           call.block_table, device=device)
     fl = torch.from_numpy(call.flags.astype(np.uint8)).to(device) if flags else None
     pc = ST.PrefillCall(batch=batch, q=ST.stored_to_tensor(call.q, device),
                         k=ST.stored_to_tensor(call.k, device), v=ST.stored_to_tensor(call.v, device),
-                        k_cache=kc, v_cache=vc, num_blocks=call.num_blocks(wl.block_size),
+                        k_cache=kc, v_cache=vc,
+                        num_blocks=call.num_blocks(wl.block_size, whole_prompt),
                         flags=fl, block_size=wl.block_size, p=wl.p, rope_theta=wl.theta,
                         window=wl.window, rows=row_sources(call, device) if compact else [],
-                        with_lse=with_lse, compact=compact)
+                        with_lse=with_lse, compact=compact,
+                        score_scope=B.UP_SCOPE_PROMPT if whole_prompt else B.UP_SCOPE_SEGMENT)
     pc.launch()
     torch.cuda.synchronize()
     return pc
@@ -118,11 +122,11 @@ def check_scores(dtype, got, ref32):
     assert np.all(g >= 0)
 
 
-def check_selection_and_compaction(wl, call, g):
+def check_selection_and_compaction(wl, call, g, whole_prompt=False):
     """Bit-exact: the oracle's top-p on the GPU scores, then the oracle's
     compaction on those keep masks, against the GPU outputs."""
     cb = g["cu_blocks"]
-    assert np.array_equal(cb, call.cu_blocks(wl.block_size))
+    assert np.array_equal(cb, call.cu_blocks(wl.block_size, whole_prompt))
     keeps = []
     for i, s in enumerate(call.segments):
         a, b = int(cb[i]), int(cb[i + 1])
@@ -139,7 +143,9 @@ def check_selection_and_compaction(wl, call, g):
         return
     from oracle.driver import row_tensors
     im, cu_out, rows_out = oracle.compact(call.cu_seqlens, [s.flagged for s in call.segments],
-                                          wl.block_size, keeps, row_tensors(call))
+                                          wl.block_size, keeps, row_tensors(call),
+                                          ctx=[s.ctx for s in call.segments],
+                                          scope="prompt" if whole_prompt else "segment")
     assert np.array_equal(g["index_map"], im)
     assert np.array_equal(g["cu_seqlens_out"], cu_out)
     for name, ref in rows_out.items():

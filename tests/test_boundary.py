@@ -56,10 +56,10 @@ def _batch(S=2, T=10, page_size=16, with_ptrs=True):
 
 
 def _attn(L, b, *, dtype=1, Hq=8, Hkv=2, D=128, ws_bytes=1 << 20, flags=None, block=64,
-          theta=1e4, scale=0.0):
+          theta=1e4, scale=0.0, scope=0):
     return L.up_prefill_attn(ctypes.byref(b) if b is not None else None, dtype, Hq, Hkv, D,
-                             FAKE, FAKE, FAKE, FAKE, FAKE, theta, 0, scale, flags, block, FAKE,
-                             FAKE, FAKE, None, FAKE, ws_bytes, None)
+                             FAKE, FAKE, FAKE, FAKE, FAKE, theta, 0, scale, flags, block, scope,
+                             FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
 
 
 def test_attention_argument_validation(L):
@@ -77,7 +77,14 @@ def test_attention_argument_validation(L):
     assert "4096" in L.up_last_error().decode()
     assert _attn(L, b, flags=FAKE, block=48) == UP_ERR_UNSUPPORTED
     assert _attn(L, b, theta=float("nan")) == UP_ERR_INVALID
-    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128, 0)
+    # whole-prompt scoring: bf16 only, needs a block table; unknown scopes refused
+    assert _attn(L, b, flags=FAKE, scope=1, dtype=0, Hq=2, Hkv=2, D=64) == UP_ERR_UNSUPPORTED
+    assert _attn(L, b, flags=FAKE, scope=3) == UP_ERR_INVALID
+    nbt = _batch()
+    nbt.block_table = None
+    assert _attn(L, nbt, flags=FAKE, scope=1) == UP_ERR_INVALID
+    assert b"block table" in L.up_last_error()
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 8, 2, 128, 0, 0)
     assert need > 16
     assert _attn(L, b, ws_bytes=need - 1) == UP_ERR_WORKSPACE
     assert b"workspace" in L.up_last_error()
@@ -89,10 +96,10 @@ def test_attention_argument_validation(L):
 def test_workspace_size_arithmetic(L):
     b = _batch(S=16, T=70000)
     # bf16: 256 packed rows per tile -> 64 positions at GQA 4; one int2 per item
-    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 0)
+    need = L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 0, 0)
     items = 16 + 8 * (math.ceil(70000 / 64) + 2 * 16 + 1)
     assert need == items
-    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128, 0) == 0
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128, 0, 0) == 0
     # scoring in bf16 adds, from a 256-byte boundary, one float per (run of
     # min(block, 64) keys, last-block row, head) for every possible block,
     # and one per (segment, last-block row, head)
@@ -100,11 +107,18 @@ def test_workspace_size_arithmetic(L):
     for B in (16, 64, 128):
         runs = (math.ceil(70000 / B) + 16) * (B // min(B, 64))
         want = base + 4 * runs * B * 32 + 4 * 16 * B * 32
-        assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, B) == want, B
-    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 48) == 0
+        assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, B, 0) == want, B
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 48, 0) == 0
     # float32 scores in its own items: no extra space
-    assert (L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 16)
-            == L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 0))
+    assert (L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 16, 0)
+            == L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 0, 0))
+    # whole-prompt scoring: the run bound also counts max_pages * 16 cached
+    # tokens per segment (the block table's width)
+    b.max_pages = 10
+    B = 64
+    runs = (math.ceil((70000 + 16 * 10 * 16) / B) + 16) * 1
+    want = base + 4 * runs * B * 32 + 4 * 16 * B * 32
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, B, 1) == want
     assert L.up_compact_workspace_bytes(16, 1100) == 8 * (1100 + 4)
     assert L.up_compact_workspace_bytes(16, 0) == 0
 
@@ -119,16 +133,17 @@ def test_select_scores_compact_validation(L):
     assert L.up_topp_select(bp, 64, None, FAKE, 0.5, FAKE, FAKE, None, None) == UP_ERR_INVALID
     assert L.up_block_scores(bp, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == UP_ERR_INVALID
     assert L.up_block_scores(bp, 8, 64, FAKE, FAKE, None, FAKE, None) == UP_ERR_INVALID
-    assert L.up_block_offsets(bp, 100, FAKE, None) == UP_ERR_UNSUPPORTED
+    assert L.up_block_offsets(bp, 100, None, 0, FAKE, None) == UP_ERR_UNSUPPORTED
+    assert L.up_block_offsets(bp, 64, FAKE, 2, FAKE, None) == UP_ERR_INVALID  # unknown scope
     rows = (Bd.UpRows * 1)(Bd.UpRows(FAKE.value, FAKE.value, 0))
-    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+    assert L.up_compact(bp, 64, FAKE, None, 0, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
                         None) == UP_ERR_INVALID  # row_bytes 0
     rows = (Bd.UpRows * 1)(Bd.UpRows(FAKE.value, FAKE.value, 8))
-    assert L.up_compact(bp, 64, FAKE, FAKE, 1, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+    assert L.up_compact(bp, 64, FAKE, None, 0, FAKE, 1, 1, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
                         None) == UP_ERR_INVALID  # fewer blocks than segments
-    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 8,
+    assert L.up_compact(bp, 64, FAKE, None, 0, FAKE, 4, 1, rows, FAKE, FAKE, FAKE, FAKE, 8,
                         None) == UP_ERR_WORKSPACE
-    assert L.up_compact(bp, 64, FAKE, FAKE, 4, 99, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+    assert L.up_compact(bp, 64, FAKE, None, 0, FAKE, 4, 99, rows, FAKE, FAKE, FAKE, FAKE, 1 << 20,
                         None) == UP_ERR_UNSUPPORTED
     assert L.up_profile_attn_events(FAKE, None) == UP_ERR_INVALID
     assert L.up_profile_attn_events(None, None) == UP_OK
@@ -196,3 +211,23 @@ def test_linear_attention_argument_validation(L):
     assert la(ks=1028) == UP_ERR_INVALID  # not a multiple of 8
     assert la(q=ctypes.c_void_p(0x1008)) == UP_ERR_INVALID
     assert la(out=ctypes.c_void_p(0x1001)) == UP_ERR_INVALID
+
+
+def test_kept_cache_slots_validation(L):
+    b = _batch()
+    bp = ctypes.byref(b)
+
+    def kc(bt=True, cu=FAKE, flags=FAKE, keep=FAKE, nb=4, slots=FAKE, cap=64, ws=1 << 20):
+        bb = _batch()
+        if not bt:
+            bb.block_table = None
+        return L.up_kept_cache_slots(ctypes.byref(bb), 64, cu, flags, keep, nb, slots, cap, FAKE,
+                                     FAKE, FAKE, ws, None)
+
+    assert kc(bt=False) == UP_ERR_INVALID
+    assert kc(flags=None) == UP_ERR_INVALID
+    assert kc(nb=1) == UP_ERR_INVALID
+    assert kc(cap=-1) == UP_ERR_INVALID
+    assert kc(ws=8) == UP_ERR_WORKSPACE
+    assert L.up_kept_cache_slots(bp, 48, FAKE, FAKE, FAKE, 4, FAKE, 64, FAKE, FAKE, FAKE,
+                                 1 << 20, None) == UP_ERR_UNSUPPORTED

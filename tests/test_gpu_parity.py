@@ -118,3 +118,54 @@ def test_gpu_bin_packed_rows_with_padding_segments():
                   Hq=8, Hkv=2, D=128, dtype="bf16", block_size=64, p=0.95, theta=500000.0,
                   scale=1.0 / np.sqrt(128.0))
     assert _run_and_check(wl)
+
+
+@pytest.mark.parametrize("B,lengths,ctxs,flags,p", [
+    (64, [88, 200, 64, 5], [512, 256, 0, 700], [True, True, True, False], 0.6),
+    (16, [40, 1, 33], [48, 160, 0], [True, True, True], 0.5),
+    (128, [300], [1024], [True], 0.7),
+])
+def test_gpu_whole_prompt_scoring(B, lengths, ctxs, flags, p):
+    """Final chunks scored over their whole prompt (cached blocks included):
+    block scores, selection and compaction by prompt block, and the KV slots
+    of the kept cached tokens, against the oracle."""
+    import torch
+    import gpu_harness as H
+    from block_sparse_token_amd import binding as Bd
+
+    wl = W.custom(seed=7000 + B, hidden_width=64, lengths=lengths, ctxs=ctxs, flags=flags, Hq=8,
+                  Hkv=2, D=128, dtype="bf16", block_size=B, p=p, theta=500000.0,
+                  scale=1.0 / np.sqrt(128.0))
+    call = wl.calls[0]
+    H.log(f"whole-prompt scoring B={B} lens={lengths} ctx={ctxs} flags={flags} p={p}")
+    ref = driver.run_workload(wl, layer2=False, scope="prompt")[0]
+    kc, vc = H.make_caches(wl)
+    pc = H.launch_call(wl, call, kc, vc, whole_prompt=True)
+    g = H.gpu_result(pc)
+    H.check_out(wl.dtype, g["out"], ref["out"], "out")
+    cb = g["cu_blocks"]
+    for i, s in enumerate(call.segments):
+        if s.flagged:
+            assert cb[i + 1] - cb[i] == -(-(s.ctx + s.n) // B)
+            H.check_scores(wl.dtype, g["scores"][cb[i]:cb[i + 1]], ref["scores"][i])
+    H.check_selection_and_compaction(wl, call, g, whole_prompt=True)
+    # kept cached tokens: the oracle's positions (on the GPU's keep masks)
+    # mapped to slots through the block table
+    keeps = [g["keep"][cb[i]:cb[i + 1]].astype(bool) for i in range(len(call.segments))]
+    pos = oracle.kept_cache_positions(flags, B, keeps, ctxs)
+    bt = call.block_table
+    want = np.concatenate([bt[i][u // 16] * 16 + u % 16 for i, u in enumerate(pos)]).astype(np.int32)
+    S = len(lengths)
+    cap = int(sum(ctxs))
+    slots = torch.full((cap + 8,), -7, dtype=torch.int32, device="cuda")
+    cu_out = torch.zeros(S + 1, dtype=torch.int32, device="cuda")
+    num = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Bd.up_kept_cache_slots(pc.batch, B, pc.cu_blocks, pc.flags, pc.keep, pc.num_blocks, slots,
+                           cu_out, num, pc.compact_ws)
+    torch.cuda.synchronize()
+    n = int(num.item())
+    assert n == len(want)
+    assert np.array_equal(slots[:n].cpu().numpy(), want)
+    assert np.all(slots[n:].cpu().numpy() == -7)
+    counts = [len(u) for u in pos]
+    assert np.array_equal(cu_out.cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]))

@@ -99,11 +99,14 @@ class Call:
     def max_ctx(self) -> int:
         return int(max(s.ctx for s in self.segments))
 
-    def num_blocks(self, block_size: int) -> int:
-        return int(sum(-(-s.n // block_size) for s in self.segments))
+    def num_blocks(self, block_size: int, whole_prompt: bool = False) -> int:
+        """Blocks of the call; with whole_prompt, a flagged segment's blocks
+        cover its cached tokens too (layout only, no arithmetic of the method)."""
+        return int(self.cu_blocks(block_size, whole_prompt)[-1])
 
-    def cu_blocks(self, block_size: int) -> np.ndarray:
-        nb = [-(-s.n // block_size) for s in self.segments]
+    def cu_blocks(self, block_size: int, whole_prompt: bool = False) -> np.ndarray:
+        nb = [-(-(s.n + (s.ctx if whole_prompt and s.flagged else 0)) // block_size)
+              for s in self.segments]
         return np.concatenate([[0], np.cumsum(nb)]).astype(np.int32)
 
 
