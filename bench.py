@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--p", type=float, default=None,
                     help="with --propagation: top-p of the selection instead of the workload's "
                          "0.95 (shows how the later-layer saving follows the kept fraction)")
+    ap.add_argument("--whole-prompt", action="store_true",
+                    help="with --workload chunked_128k: earlier chunks unscored, the final chunk "
+                         "scores every block of the prompt (cached ones included)")
     ap.add_argument("--propagation", action="store_true",
                     help="time one later layer's linear maps on all vs the kept tokens of the "
                          "headline batch")
@@ -97,15 +100,24 @@ def run_other_workload(args):
     wl = W.make(args.workload)
     kc, vc = WD.make_caches(wl)
     calls = []
-    for call in wl.calls:
+    whole = args.whole_prompt
+    if whole and args.workload != "chunked_128k":
+        raise SystemExit("--whole-prompt applies to chunked_128k (one prompt in chunks)")
+    for ci, call in enumerate(wl.calls):
         batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
                               call.block_table)
-        flags = torch.from_numpy(call.flags.astype(np.uint8)).cuda()
+        final = ci == len(wl.calls) - 1
+        fl = call.flags.astype(np.uint8)
+        if whole:  # earlier chunks pass through; the final one scores the prompt
+            fl = fl * np.uint8(final)
+        flags = torch.from_numpy(fl).cuda()
         calls.append((call, ST.PrefillCall(
             batch=batch, q=WD.stored_to_tensor(call.q), k=WD.stored_to_tensor(call.k),
             v=WD.stored_to_tensor(call.v), k_cache=kc, v_cache=vc,
-            num_blocks=call.num_blocks(wl.block_size), flags=flags, block_size=wl.block_size,
-            p=wl.p, rope_theta=wl.theta, window=wl.window, rows=WD.row_sources(call))))
+            num_blocks=call.num_blocks(wl.block_size, whole and final), flags=flags,
+            block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, window=wl.window,
+            rows=WD.row_sources(call),
+            score_scope=B.UP_SCOPE_PROMPT if whole and final else B.UP_SCOPE_SEGMENT)))
     layer2 = None
     if wl.layer2:
         pc = calls[0][1]
@@ -190,6 +202,19 @@ def run_other_workload(args):
     achieved = flops / (attn * 1e-3) / 1e12
     tokens = T_all
     res_extra = {}
+    if whole:
+        pc_f = calls[-1][1]
+        nbp = int(pc_f.cu_blocks[-1].item())
+        keep = pc_f.keep[:nbp].cpu().numpy().astype(bool)
+        sc = pc_f.scores[:nbp].cpu().numpy()
+        hb = -(-wl.heavy_prefix // wl.block_size)  # blocks holding the heavy-hitter cluster
+        res_extra["whole_prompt"] = {
+            "prompt_blocks": nbp, "kept_blocks": int(keep.sum()),
+            "cluster_blocks": hb, "cluster_blocks_kept": int(keep[:hb].sum()),
+            "other_blocks_kept": int(keep[hb:].sum()),
+            "mean_score_cluster": float(sc[:hb].mean()), "mean_score_other": float(sc[hb:].mean()),
+            "kept_cached_tokens": int(pc_f.num_kept_slots.item()),
+            "kept_own_tokens": int(pc_f.num_kept.item())}
     if args.workload == "mixed_decode_prefill":
         c = calls[0][0]
         dec = [i for i, s in enumerate(c.segments) if not s.flagged]

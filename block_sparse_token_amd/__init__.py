@@ -7,8 +7,13 @@ Importing this package does not touch the GPU.
 """
 from .binding import (  # noqa: F401
     EXPORTED,
+    UP_ACT_NONE,
+    UP_ACT_SWIGLU,
+    UP_SCOPE_PROMPT,
+    UP_SCOPE_SEGMENT,
     Batch,
     UniprefillError,
+    interleave_gate_up,
     lib,
     up_attn_workspace_bytes,
     up_block_offsets,
@@ -16,6 +21,9 @@ from .binding import (  # noqa: F401
     up_check_batch,
     up_compact,
     up_compact_workspace_bytes,
+    up_kept_cache_slots,
+    up_linear_attn_bf16,
+    up_linear_bf16,
     up_prefill_attn,
     up_topp_select,
     up_version,

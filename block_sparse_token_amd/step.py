@@ -88,6 +88,12 @@ class PrefillCall:
         self.compact_ws = torch.empty(B.up_compact_workspace_bytes(S, NB), dtype=torch.uint8,
                                       device=dev)
         self.rows_out = {name: torch.empty_like(src) for name, src in self.rows}
+        if self.score_scope == B.UP_SCOPE_PROMPT:
+            # KV slots of the kept cached tokens (at most every cached token)
+            cap = S * self.batch.max_pages * self.batch.page_size
+            self.kept_slots = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+            self.cu_kept_slots = torch.empty(S + 1, dtype=torch.int32, device=dev)
+            self.num_kept_slots = torch.empty(1, dtype=torch.int32, device=dev)
 
     # individual stages (each one library call, or two for scoring)
     def attention(self, stream=None):
@@ -113,6 +119,10 @@ class PrefillCall:
         B.up_compact(self.batch, self.block_size, self.cu_blocks, self.keep, self.num_blocks, rows,
                      self.index_map, self.cu_seqlens_out, self.num_kept, self.compact_ws,
                      score_flags=self.flags, score_scope=self.score_scope, stream=stream)
+        if self.score_scope == B.UP_SCOPE_PROMPT:
+            B.up_kept_cache_slots(self.batch, self.block_size, self.cu_blocks, self.flags, self.keep,
+                                  self.num_blocks, self.kept_slots, self.cu_kept_slots,
+                                  self.num_kept_slots, self.compact_ws, stream)
 
     def launch(self, stream=None):
         self.attention(stream)

@@ -135,6 +135,7 @@ class Workload:
     device_cache_ctx: dict = field(default_factory=dict)  # prompt id -> c
     layer2: dict | None = None  # second (sliding-window) layer settings
     seed: int = 0
+    heavy_prefix: int = 0  # tokens of the leading heavy-hitter cluster, if any
 
     @property
     def G(self) -> int:
@@ -313,7 +314,8 @@ def config_chunked_128k(seed: int = 3, total: int = 131072, chunk: int = 8192) -
     calls = _finish_calls(sched, qs, ks, vs, hs, pages)
     return Workload(name="chunked_128k", dtype="bf16", Hq=32, Hkv=8, D=128, block_size=128, p=0.9,
                     theta=500000.0, window=0, hidden_width=4096, num_pages=npages,
-                    prompt_pages=pages, prompt_len=plen, calls=calls, seed=seed)
+                    prompt_pages=pages, prompt_len=plen, calls=calls, seed=seed,
+                    heavy_prefix=nh * GROUP)
 
 
 def config_mixed_decode_prefill(seed: int = 4, n_decode: int = 256, budget: int = 8192,
