@@ -41,7 +41,9 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(
       s = lo;
       const int n = cu_seqlens[s + 1] - cu_seqlens[s];
       const int i0 = (k - cu_blocks[s]) * B - bo.of(s);  // first own row of the block
-      if (cached) v = keep[k] && i0 < 0 ? B : 0;
+      // (a cached block holds min(B, -i0) cached tokens; B whenever the
+      // cached length is on the block grid, as whole-prompt scoring requires)
+      if (cached) v = keep[k] && i0 < 0 ? min(B, -i0) : 0;
       else v = keep[k] && i0 >= 0 ? min(B, n - i0) : 0;
       block_seg[k] = s;
     }
@@ -148,8 +150,10 @@ __global__ __launch_bounds__(256) void kept_cache_slots_kernel(
   if (k >= cu_blocks[S] || !keep[k]) return;
   const int s = block_seg[k];
   const int u0 = (k - cu_blocks[s]) * B;
-  if (u0 >= bo.of(s)) return;  // a block of the segment's own rows
-  for (int r = threadIdx.x; r < B; r += 256) {
+  const int c = bo.of(s);
+  if (u0 >= c) return;  // a block of the segment's own rows
+  // only cached tokens (u < c), so the block table is read inside its prefix
+  for (int r = threadIdx.x; r < min(B, c - u0); r += 256) {
     const int u = u0 + r, d = block_out[k] + r;
     if (d < slots_cap)
       slots[d] = block_table[(long)s * max_pages + (u >> 4)] * kPageSize + (u & (kPageSize - 1));
