@@ -82,7 +82,8 @@ def prompt_kv_before(wl, call_index, pid):
 
 
 def sampled_segment(wl, call, si, rows, *, cached=None, theta=None, window=None,
-                    score=False, q=None, k=None, v=None, positions=None, cu=None, threads=None):
+                    score=False, q=None, k=None, v=None, positions=None, cu=None, threads=None,
+                    scope="segment"):
     """Oracle outputs of segment ``si`` for local query rows ``rows`` and,
     with ``score``, the segment's float32 block scores.
 
@@ -114,6 +115,6 @@ def sampled_segment(wl, call, si, rows, *, cached=None, theta=None, window=None,
     res = {"rows": rows, "out": out, "lse": lse}
     if score:
         q_all = apply_rope(qa, pos, theta)
-        m = block_mass(q_all, keys, pos, k_pos, c, n, wl.block_size, window)
+        m = block_mass(q_all, keys, pos, k_pos, c, n, wl.block_size, window, scope=scope)
         res["scores"] = normalise_scores(m).astype(np.float32)
     return res

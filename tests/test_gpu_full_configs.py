@@ -76,6 +76,40 @@ def test_gpu_chunked_128k_full():
     H.log("chunked_128k: ok")
 
 
+def test_gpu_chunked_128k_whole_prompt_full():
+    """The 131072-token prompt with only its final chunk scored, over the
+    whole prompt: all 1024 block scores, sampled output rows, selection and
+    compaction by prompt block, and the kept cached tokens' KV slots."""
+    import gpu_harness as H
+    from block_sparse_token_amd import binding as Bd
+    wl = W.make("chunked_128k")
+    kc, vc = H.make_caches(wl)
+    last = len(wl.calls) - 1
+    for ci, call in enumerate(wl.calls[:-1]):
+        H.launch_call(wl, call, kc, vc, flags=False, compact=False)
+    call = wl.calls[last]
+    H.log(f"chunked_128k whole prompt: final call ctx={call.segments[0].ctx}")
+    pc = H.launch_call(wl, call, kc, vc, whole_prompt=True)
+    g = H.gpu_result(pc)
+    kk, vv, pp = driver.prompt_kv_before(wl, last, call.segments[0].prompt)
+    cached = (oracle.apply_rope(kk, pp, wl.theta), vv)
+    s = call.segments[0]
+    rows = _rows(np.random.default_rng(3), s.n, 4)
+    r = driver.sampled_segment(wl, call, 0, rows, cached=cached, score=True, scope="prompt")
+    H.check_out(wl.dtype, g["out"][np.asarray(rows)], r["out"], f"final chunk rows {rows}")
+    cb = g["cu_blocks"]
+    assert cb[1] - cb[0] == 1024
+    H.check_scores(wl.dtype, g["scores"][cb[0]:cb[1]], r["scores"])
+    H.check_selection_and_compaction(wl, call, g, whole_prompt=True)
+    keep = g["keep"][cb[0]:cb[1]].astype(bool)
+    pos = oracle.kept_cache_positions([True], wl.block_size, [keep], [s.ctx])[0]
+    want = (call.block_table[0][pos // 16] * 16 + pos % 16).astype(np.int32)
+    n = int(pc.num_kept_slots.item())
+    assert n == len(want)
+    assert np.array_equal(pc.kept_slots[:n].cpu().numpy(), want)
+    H.log(f"chunked_128k whole prompt: ok ({int(keep.sum())} of 1024 blocks kept)")
+
+
 def test_gpu_mixed_decode_prefill_full():
     import gpu_harness as H
     wl = W.make("mixed_decode_prefill")
