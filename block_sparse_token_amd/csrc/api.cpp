@@ -78,10 +78,13 @@ bool debug_checks() {
   return v && atoi(v) != 0;
 }
 
-up_status run_check(const up_batch* b, int32_t num_pages, int32_t* err, hipStream_t st) {
+// grid > 0: also check that every segment flagged in score_flags has a
+// ctx_len that is a multiple of grid (whole-prompt scoring).
+up_status run_check(const up_batch* b, int32_t num_pages, int32_t* err, hipStream_t st,
+                    const uint8_t* score_flags = nullptr, int grid = 0) {
   hipError_t e = up::launch_check_batch(b->cu_seqlens, b->ctx_lens, b->positions,
-                                        b->slot_mapping, b->block_table, b->num_seqs,
-                                        b->num_tokens, b->max_pages, num_pages, err, st);
+                                        b->slot_mapping, b->block_table, score_flags, b->num_seqs,
+                                        b->num_tokens, b->max_pages, num_pages, grid, err, st);
   if (e != hipSuccess) return device_status(e, "batch check launch");
   int32_t bits = 0;
   e = hipMemcpyAsync(&bits, err, sizeof bits, hipMemcpyDeviceToHost, st);
@@ -95,9 +98,10 @@ up_status run_check(const up_batch* b, int32_t num_pages, int32_t* err, hipStrea
                                "positions not increasing inside a segment or below ctx_len",
                                "slot out of range",
                                "page id out of range",
-                               "block table too short or missing for cached tokens"};
+                               "block table too short or missing for cached tokens",
+                               "a scored segment's ctx_len is not a multiple of block_size"};
   std::string msg = "batch check failed:";
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 9; ++i)
     if (bits & (1 << i)) {
       msg += " ";
       msg += what[i];
@@ -287,7 +291,8 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
 
   hipStream_t s = as_stream(stream);
   if (debug_checks()) {
-    st = run_check(batch, 0, (int32_t*)workspace, s);
+    const bool prompt = score_flags && score_scope == UP_SCOPE_PROMPT;
+    st = run_check(batch, 0, (int32_t*)workspace, s, score_flags, prompt ? block_size : 0);
     if (st) return st;
   }
   const bool bf16 = dtype == UP_BF16;

@@ -91,10 +91,13 @@ constexpr int kCheckPositions = 1 << 4;   // not strictly increasing, or first <
 constexpr int kCheckSlots = 1 << 5;       // slot < -1 or beyond the page pool
 constexpr int kCheckPages = 1 << 6;       // page id < 0 or beyond the page pool
 constexpr int kCheckBlockTable = 1 << 7;  // table too short for ctx + n, or missing
+constexpr int kCheckBlockGrid = 1 << 8;   // scored ctx_len not a multiple of `grid`
+// grid > 0 (with score_flags): the whole-prompt scoring precondition
 hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens,
                               const int32_t* positions, const int32_t* slot_mapping,
-                              const int32_t* block_table, int S, int T, int max_pages,
-                              int num_pages, int32_t* err, hipStream_t st);
+                              const int32_t* block_table, const uint8_t* score_flags, int S,
+                              int T, int max_pages, int num_pages, int grid, int32_t* err,
+                              hipStream_t st);
 hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st);
 hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);

@@ -147,8 +147,9 @@ __global__ __launch_bounds__(256) void check_batch_kernel(const int32_t* __restr
                                                           const int32_t* __restrict__ positions,
                                                           const int32_t* __restrict__ slot_mapping,
                                                           const int32_t* __restrict__ block_table,
+                                                          const uint8_t* __restrict__ score_flags,
                                                           int S, int T, int max_pages,
-                                                          int num_pages, int32_t* err) {
+                                                          int num_pages, int grid, int32_t* err) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= S) return;
   int bits = 0;
@@ -158,6 +159,8 @@ __global__ __launch_bounds__(256) void check_batch_kernel(const int32_t* __restr
   if (cu_seqlens[s + 1] - cu_seqlens[s] < 1) bits |= kCheckSegment;
   const int c = ctx_lens[s];
   if (c < 0) bits |= kCheckCtx;
+  // whole-prompt scoring: a scored segment's cached tokens fill whole blocks
+  if (grid > 0 && score_flags && score_flags[s] && c % grid) bits |= kCheckBlockGrid;
   for (int t = a; t < b; ++t) {
     const int p = positions[t];
     if (t == a ? p < c : p <= positions[t - 1]) bits |= kCheckPositions;
@@ -180,12 +183,13 @@ __global__ __launch_bounds__(256) void check_batch_kernel(const int32_t* __restr
 
 hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens,
                               const int32_t* positions, const int32_t* slot_mapping,
-                              const int32_t* block_table, int S, int T, int max_pages,
-                              int num_pages, int32_t* err, hipStream_t st) {
+                              const int32_t* block_table, const uint8_t* score_flags, int S,
+                              int T, int max_pages, int num_pages, int grid, int32_t* err,
+                              hipStream_t st) {
   hipLaunchKernelGGL(check_zero_kernel, dim3(1), dim3(64), 0, st, err);
   hipLaunchKernelGGL(check_batch_kernel, dim3((S + 255) / 256), dim3(256), 0, st, cu_seqlens,
-                     ctx_lens, positions, slot_mapping, block_table, S, T, max_pages, num_pages,
-                     err);
+                     ctx_lens, positions, slot_mapping, block_table, score_flags, S, T, max_pages,
+                     num_pages, grid, err);
   return hipGetLastError();
 }
 

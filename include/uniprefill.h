@@ -350,7 +350,9 @@ up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream);
  * With the environment variable UP_DEBUG_CHECKS set to a non-zero integer
  * (read on every call), up_prefill_attn runs this check (num_pages = 0,
  * the workspace's first word as err_word) before it launches anything, and
- * returns its status if the batch fails it.
+ * returns its status if the batch fails it; with score_scope
+ * UP_SCOPE_PROMPT it also checks that every scored segment's ctx_len is a
+ * multiple of block_size.
  */
 up_status up_check_batch(const up_batch* batch, int32_t num_pages, int32_t* err_word,
                          void* stream);

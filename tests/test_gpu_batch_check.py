@@ -136,3 +136,35 @@ def test_gpu_debug_checks_hook_in_attention():
             del os.environ["UP_DEBUG_CHECKS"]
         else:
             os.environ["UP_DEBUG_CHECKS"] = old
+
+
+def test_gpu_debug_checks_whole_prompt_block_grid():
+    """Whole-prompt scoring needs every scored segment's ctx_len on the block
+    grid: the debug hook passes a batch whose only off-grid ctx_len belongs
+    to an unscored segment (same results as without the hook) and names the
+    violation when a scored one is off the grid."""
+    import gpu_harness as H
+    good = W.custom(seed=7064, hidden_width=64, lengths=[88, 200, 64, 5], ctxs=[512, 256, 0, 700],
+                    flags=[True, True, True, False], Hq=8, Hkv=2, D=128, dtype="bf16",
+                    block_size=64, p=0.6, theta=500000.0)
+    bad = W.custom(seed=7065, hidden_width=64, lengths=[40, 70, 5], ctxs=[0, 33, 64], Hq=8, Hkv=2,
+                   D=128, dtype="bf16", block_size=32, p=0.9, theta=500000.0)
+    kc, vc = H.make_caches(good)
+    ref = H.gpu_result(H.launch_call(good, good.calls[0], kc.clone(), vc.clone(),
+                                     whole_prompt=True))
+    old = os.environ.get("UP_DEBUG_CHECKS")
+    os.environ["UP_DEBUG_CHECKS"] = "1"
+    try:
+        got = H.gpu_result(H.launch_call(good, good.calls[0], kc.clone(), vc.clone(),
+                                         whole_prompt=True))
+        for key in ("out", "scores", "keep", "index_map"):
+            assert np.array_equal(np.asarray(got[key]).view(np.uint8),
+                                  np.asarray(ref[key]).view(np.uint8)), key
+        kb, vb = H.make_caches(bad)
+        with pytest.raises(Bd.UniprefillError, match="not a multiple of block_size"):
+            H.launch_call(bad, bad.calls[0], kb, vb, whole_prompt=True)
+    finally:
+        if old is None:
+            del os.environ["UP_DEBUG_CHECKS"]
+        else:
+            os.environ["UP_DEBUG_CHECKS"] = old
