@@ -508,6 +508,28 @@ def run_propagation(args):
                                                        "linear.hip")),
                          "linear_bf16_later_layer_kernel_stats.md")},
     }
+    # reference point, not part of the path: the vendor GEMM library
+    # (torch.matmul, hipBLASLt) on the same bf16 operands and all rows; the
+    # gated map without the SwiGLU epilogue (its output is twice as wide)
+    lib_maps = {"qkv": (x_all, w_qkv), "o": (attn.view(T, H), w_o),
+                "gate_up_swiglu": (x_all, w_gu), "down": (hmid, w_down)}
+    library = {}
+    for name, (inp, w) in lib_maps.items():
+        wt = w.t()
+        for _ in range(args.warmup):
+            torch.matmul(inp, wt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            torch.matmul(inp, wt)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        library[name] = {"ms_all": ms, "TFLOP/s_all": res_maps[name]["flops_all"] / (ms * 1e-3) / 1e12,
+                         "ours_over_library_time": res_maps[name]["ms_all"] / ms}
+    res["library_gemm"] = {"what": "torch.matmul (hipBLASLt) on the same operands, all rows; "
+                                   "gate/up without the SwiGLU epilogue; reference only",
+                           "maps": library}
     if not args.no_cpu_baseline:
         # the oracle's four maps on the first kept rows, float64 on this host
         n = 512
