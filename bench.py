@@ -353,6 +353,53 @@ def headline_call(torch, p=None):
     return wl, call, pc
 
 
+def library_attention(torch, wl, call, pc, steps):
+    """Reference point outside the path: PyTorch's fused flash attention
+    (scaled_dot_product_attention held to its flash backend, so it never
+    falls back to the unfused math) on the same q, k, v, one causal call per
+    prompt (it has no packed variable-length form), timed back to back; and
+    the longest prompt alone, which fills the chip by itself.  No RoPE, no
+    paged cache and no block mass there."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    try:
+        cu = [int(c) for c in call.cu_seqlens]
+        segs = []
+        for a, b in zip(cu[:-1], cu[1:]):
+            segs.append(tuple(x[a:b].transpose(0, 1).unsqueeze(0).contiguous()
+                              for x in (pc.q, pc.k, pc.v)))
+        longest = max(range(len(segs)), key=lambda i: cu[i + 1] - cu[i])
+
+        def run(idx):
+            for i in idx:
+                q, k, v = segs[i]
+                F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+
+        out = {"what": "torch scaled_dot_product_attention, flash backend only, one causal call "
+                       "per prompt on the same q/k/v (no RoPE, cache or block mass); reference "
+                       "only, not part of the path"}
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for name, idx in (("all_prompts_serial", list(range(len(segs)))),
+                              ("longest_prompt", [longest])):
+                run(idx)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(steps):
+                    run(idx)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / steps
+                pairs = sum((cu[i + 1] - cu[i]) * (cu[i + 1] - cu[i] + 1) / 2 for i in idx)
+                out[name] = {"prompts": len(idx), "ms": ms,
+                             "TFLOP/s": 4.0 * wl.D * wl.Hq * pairs / (ms * 1e-3) / 1e12}
+        del segs
+        return out
+    except Exception as ex:  # a reference only: report, never fail the bench
+        return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
+
+
 def cpu_baseline(wl, call, budget_s):
     """Time the oracle on whole prompts of the batch, picked near the
     token-weighted mean length (attention cost per token grows with length),
@@ -828,6 +875,7 @@ def main():
                                      "frac_cache_flushed": b / (fl_ms[k] * 1e-3) / 1e9 /
                                      PEAK_HBM_GBS})
     res["roofline"]["avg_ms_cache_flushed"] = attn_fl
+    res["library_attention"] = library_attention(torch, wl, call, pc, min(K, 5))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
