@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     up_compact_workspace_bytes,
     up_kept_cache_slots,
     up_linear_attn_bf16,
+    up_linear_attn_workspace_bytes,
     up_linear_bf16,
     up_prefill_attn,
     up_topp_select,

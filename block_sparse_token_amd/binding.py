@@ -74,6 +74,10 @@ def lib():
             "up_linear_attn_bf16": (c_i32, [c_vp, c_i32, c_vp, ctypes.c_int64, c_vp,
                                             ctypes.c_int64, c_vp, ctypes.c_int64, c_i32, c_i32,
                                             c_i32, c_vp, c_vp]),
+            "up_linear_attn_workspace_bytes": (c_size, [c_i32, c_i32, c_i32]),
+            "up_linear_attn_bf16_parts": (c_i32, [c_vp, c_i32, c_i32, c_vp, ctypes.c_int64, c_vp,
+                                                  ctypes.c_int64, c_vp, ctypes.c_int64, c_i32,
+                                                  c_i32, c_i32, c_vp, c_vp, c_size, c_vp]),
             "up_linear_bf16": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_vp]),
             "up_compact": (c_i32, [bp, c_i32, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32,
                                    ctypes.POINTER(UpRows), c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
@@ -91,7 +95,8 @@ def lib():
 EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspace_bytes",
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
-            "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16", "up_kept_cache_slots"]
+            "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16", "up_kept_cache_slots",
+            "up_linear_attn_workspace_bytes", "up_linear_attn_bf16_parts"]
 
 
 def _check(st: int, what: str):
@@ -273,11 +278,17 @@ def interleave_gate_up(w_gate, w_up):
                        dim=1).reshape(2 * F, K).contiguous()
 
 
-def up_linear_attn_bf16(cu_seqlens, q, k, v, out, stream=None):
+def up_linear_attn_workspace_bytes(rows, num_seqs, Hq):
+    return int(lib().up_linear_attn_workspace_bytes(int(rows), int(num_seqs), int(Hq)))
+
+
+def up_linear_attn_bf16(cu_seqlens, q, k, v, out, workspace=None, stream=None):
     """Causal linear attention (phi = elu + 1) over each segment of
     ``cu_seqlens``.  q [rows, Hq, D] and k, v [rows, Hkv, D] bfloat16 views
     whose rows may be strided (e.g. column ranges of one projection output,
-    ``qkv[:, :Hq*D].view(rows, Hq, D)``); out [rows, Hq, D] contiguous."""
+    ``qkv[:, :Hq*D].view(rows, Hq, D)``); out [rows, Hq, D] contiguous.
+    With ``workspace`` (a uint8 GPU tensor of up_linear_attn_workspace_bytes
+    bytes) the chunk-parallel entry point runs instead."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.device.type != "cuda":
             raise UniprefillError(f"{name} must be a 3-D bfloat16 GPU tensor")
@@ -289,6 +300,14 @@ def up_linear_attn_bf16(cu_seqlens, q, k, v, out, stream=None):
     Hkv = k.shape[1]
     if k.shape != v.shape or k.shape[0] != rows or out.shape != q.shape:
         raise UniprefillError("q, k, v and out shapes do not match")
+    if workspace is not None:
+        _check(lib().up_linear_attn_bf16_parts(
+            _p(cu_seqlens), cu_seqlens.numel() - 1, rows, ctypes.c_void_p(q.data_ptr()),
+            q.stride(0), ctypes.c_void_p(k.data_ptr()), k.stride(0),
+            ctypes.c_void_p(v.data_ptr()), v.stride(0), Hq, Hkv, D, _p(out), _p(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream)),
+            "up_linear_attn_bf16_parts")
+        return
     _check(lib().up_linear_attn_bf16(_p(cu_seqlens), cu_seqlens.numel() - 1,
                                      ctypes.c_void_p(q.data_ptr()), q.stride(0),
                                      ctypes.c_void_p(k.data_ptr()), k.stride(0),

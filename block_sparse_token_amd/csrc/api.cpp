@@ -156,10 +156,11 @@ up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return device_status(up::launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak copy launch");
 }
 
-up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
-                              int64_t q_stride, const void* k, int64_t k_stride, const void* v,
-                              int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                              void* out, void* stream) {
+namespace {
+up_status check_linear_attn(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
+                            int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                            int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            void* out) {
   if (!cu_seqlens || !q || !k || !v || !out)
     return fail(UP_ERR_INVALID, "cu_seqlens, q, k, v and out must be non-NULL");
   if (num_seqs <= 0 || num_seqs > 65535)
@@ -173,8 +174,47 @@ up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const
   if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) & 15)
     return fail(UP_ERR_INVALID, "q, k and v must be 16-byte aligned");
   if (((uintptr_t)out) & 1) return fail(UP_ERR_INVALID, "out must be 2-byte aligned");
-  return device_status(up::launch_linear_attn_bf16(cu_seqlens, num_seqs, q, q_stride, k, k_stride,
-                                                   v, v_stride, Hq, Hkv, out, as_stream(stream)),
+  return UP_OK;
+}
+}  // namespace
+
+up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
+                              int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                              int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              void* out, void* stream) {
+  up_status st = check_linear_attn(cu_seqlens, num_seqs, q, q_stride, k, k_stride, v, v_stride,
+                                   Hq, Hkv, head_dim, out);
+  if (st) return st;
+  return device_status(up::launch_linear_attn_bf16(cu_seqlens, num_seqs, 0, q, q_stride, k,
+                                                   k_stride, v, v_stride, Hq, Hkv, out, nullptr,
+                                                   as_stream(stream)),
+                       "linear attention launch");
+}
+
+size_t up_linear_attn_workspace_bytes(int32_t rows, int32_t num_seqs, int32_t Hq) {
+  if (rows < 0 || num_seqs <= 0 || Hq <= 0) return 0;
+  return up::linear_attn_workspace_bytes(rows, num_seqs, Hq);
+}
+
+up_status up_linear_attn_bf16_parts(const int32_t* cu_seqlens, int32_t num_seqs, int32_t rows,
+                                    const void* q, int64_t q_stride, const void* k,
+                                    int64_t k_stride, const void* v, int64_t v_stride, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  up_status st = check_linear_attn(cu_seqlens, num_seqs, q, q_stride, k, k_stride, v, v_stride,
+                                   Hq, Hkv, head_dim, out);
+  if (st) return st;
+  if (rows < 0) return fail(UP_ERR_INVALID, "rows must be >= 0 (got %d)", rows);
+  if ((int64_t)rows / 1024 + num_seqs + 1 > 65535)
+    return fail(UP_ERR_UNSUPPORTED, "rows / 1024 + num_seqs + 1 must be <= 65535");
+  if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace) & 15) return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
+  const size_t need = up::linear_attn_workspace_bytes(rows, num_seqs, Hq);
+  if (workspace_bytes < need)
+    return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return device_status(up::launch_linear_attn_bf16(cu_seqlens, num_seqs, rows, q, q_stride, k,
+                                                   k_stride, v, v_stride, Hq, Hkv, out, workspace,
+                                                   as_stream(stream)),
                        "linear attention launch");
 }
 

@@ -101,9 +101,14 @@ hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens
 hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st);
 hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
-hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void* q, long q_stride,
-                                   const void* k, long k_stride, const void* v, long v_stride,
-                                   int Hq, int Hkv, void* out, hipStream_t st);
+// ws NULL: one workgroup per (query head, segment); else the
+// chunk-parallel form over parts, ws of linear_attn_workspace_bytes(rows,
+// S, Hq) bytes
+size_t linear_attn_workspace_bytes(int rows, int S, int Hq);
+hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, int rows, const void* q,
+                                   long q_stride, const void* k, long k_stride, const void* v,
+                                   long v_stride, int Hq, int Hkv, void* out, void* ws,
+                                   hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int rows_cap,
                               const int32_t* rows_dev, int N, int K, int act, hipStream_t st);
 hipError_t launch_block_offsets(const int32_t* cu_seqlens, const BlockOrigin& bo, int S, int block_size,

@@ -60,6 +60,18 @@ __device__ inline int off128(int r, int e) { return r * 128 + ((((e >> 3) ^ ((r 
 
 __device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// Chunk-parallel form (when the caller passes a workspace): each segment
+// is cut into parts of kPart tokens.  Part p of segment s has the slot
+// cu_seqlens[s] / kPart + s + p, distinct for all parts and below
+// rows / kPart + S + 1.  Pass 1 runs every part but a segment's last in
+// parallel and stores the part's own (S, z) sums; pass 2 turns them, per
+// segment and head, into running sums over the parts (inclusive); pass 3
+// runs every part in parallel from the running sum of the parts before it
+// and writes the outputs.  The recurrence is linear in (S, z), so the
+// result is the same up to the order of float32 additions.
+constexpr int kPart = 1024;
+constexpr int kState = kD * kD + kD;  // floats of (S, z) per part and query head
+
 struct LinAttnArgs {
   const int32_t* cu_seqlens;
   const uint16_t* q;
@@ -68,26 +80,64 @@ struct LinAttnArgs {
   long q_stride, k_stride, v_stride;  // elements between consecutive tokens
   int Hq, Hkv;
   uint16_t* out;  // [rows, Hq, 128]
+  float* ws;      // [slots, Hq, kState] (chunk-parallel form)
+  int S;
 };
+
+__device__ inline int part_slot(const int32_t* cu, int s) { return cu[s] / kPart + s; }
 
 __device__ inline float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// MODE 0: whole segments (blockIdx.y = segment).  MODE 1: part states
+// (blockIdx.y = slot; no outputs).  MODE 2: part outputs from the running
+// sums of the parts before.
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int h = blockIdx.x, s = blockIdx.y;
+  const int h = blockIdx.x;
   const int g = h / (a.Hq / a.Hkv);
-  const int t_begin = a.cu_seqlens[s], t_end = a.cu_seqlens[s + 1];
+  int t_begin, t_end, slot = 0, p = 0;
+  if (MODE == 0) {
+    t_begin = a.cu_seqlens[blockIdx.y];
+    t_end = a.cu_seqlens[blockIdx.y + 1];
+  } else {
+    // the segment owning this slot: the last one whose first slot is <= it
+    slot = blockIdx.y;
+    int lo = 0, hi = a.S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (part_slot(a.cu_seqlens, mid) <= slot) lo = mid;
+      else hi = mid - 1;
+    }
+    p = slot - part_slot(a.cu_seqlens, lo);
+    const int a0 = a.cu_seqlens[lo], n = a.cu_seqlens[lo + 1] - a0;
+    const int np = (n + kPart - 1) / kPart;
+    // a slot between two segments' parts, or a segment's last part (whose
+    // sums no later part reads)
+    if (p < 0 || p >= np || (MODE == 1 && p == np - 1)) return;
+    t_begin = a0 + p * kPart;
+    t_end = min(a0 + n, t_begin + kPart);
+  }
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t L0 = lds_addr_of(lds);
 
-  // z starts at zero
-  if (tid < kD * 4 / 16) *(u32x4*)(lds + ZF + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  // S and z start at zero, or at the running sums of the parts before
   f32x16 sacc[4];  // S[32i + row][32w + col] blocks, i = d_in block
+  if (MODE == 2 && p > 0) {
+    const float* prev = a.ws + ((long)(slot - 1) * a.Hq + h) * kState;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sacc[i][e] = 0.f;
+      for (int e = 0; e < 16; ++e) sacc[i][e] = prev[(i * 16 + e) * kThreads + tid];
+    if (tid < kD) ((float*)(lds + ZF))[tid] = prev[kD * kD + tid];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[i][e] = 0.f;
+    if (tid < kD * 4 / 16) *(u32x4*)(lds + ZF + tid * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
   __syncthreads();
 
   // the chunk's raw q, k, v rows: thread tid handles (row p / 16, 16-byte
@@ -100,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
       rq[i] = rk[i] = rv[i] = u32x4{0u, 0u, 0u, 0u};
       if (t0 + r < t_end) {
         const long t = t0 + r;
-        rq[i] = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
+        if (MODE != 1) rq[i] = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
         rk[i] = *(const u32x4*)(a.k + t * a.k_stride + (long)g * kD + c * 8);
         rv[i] = *(const u32x4*)(a.v + t * a.v_stride + (long)g * kD + c * 8);
       }
@@ -125,8 +175,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
         fq[e] = ok ? (__bf16)phi(bf2f(q16[e])) : (__bf16)0.f;
         fk[e] = ok ? (__bf16)phi(bf2f(k16[e])) : (__bf16)0.f;
       }
-      *(bf16x8*)(lds + QF + off256(r, c * 8)) = fq;
-      *(bf16x8*)(lds + KF + off256(r, c * 8)) = fk;
+      if (MODE != 1) {
+        *(bf16x8*)(lds + QF + off256(r, c * 8)) = fq;
+        *(bf16x8*)(lds + KF + off256(r, c * 8)) = fk;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         *(__bf16*)(lds + KT + off128(c * 8 + e, r)) = fk[e];
@@ -135,6 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
     }
     __syncthreads();
 
+    if (MODE != 1) {
     // (b) wave w: A block (rows 32 (w >> 1).., keys 32 (w & 1)..), masked,
     // to LDS in bf16
     {
@@ -243,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
             }
           }
     }
+    }  // MODE != 1
 
     // (e) this chunk's phi(K)^T V into S (registers; wave w's columns), and
     // its keys into z once every wave has read z for the denominators
@@ -269,13 +323,46 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
     }
     __syncthreads();
   }
+  if (MODE == 1) {
+    float* own = a.ws + ((long)slot * a.Hq + h) * kState;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) own[(i * 16 + e) * kThreads + tid] = sacc[i][e];
+    if (tid < kD) own[kD * kD + tid] = ((const float*)(lds + ZF))[tid];
+  }
+}
+
+// pass 2: per (query head, segment), the part sums of parts 0..np-2 become
+// running sums (inclusive), in part order; slots at or past `slots` (a
+// batch that breaks cu_seqlens[S] <= rows) are left alone
+__global__ __launch_bounds__(256) void linear_attn_prefix_kernel(const int32_t* __restrict__ cu,
+                                                                 float* ws, int Hq, int slots) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int a0 = cu[s], n = cu[s + 1] - a0;
+  const int np = (n + kPart - 1) / kPart;
+  const long first = part_slot(cu, s);
+  if (np < 3 || first < 0 || first + np - 2 >= slots) return;
+  for (int e = threadIdx.x; e < kState; e += 256) {
+    float r = 0.f;
+    for (int q = 0; q < np - 1; ++q) {
+      float* x = ws + ((first + q) * Hq + h) * kState + e;
+      r += *x;
+      *x = r;
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void* q, long q_stride,
-                                   const void* k, long k_stride, const void* v, long v_stride,
-                                   int Hq, int Hkv, void* out, hipStream_t st) {
+size_t linear_attn_workspace_bytes(int rows, int S, int Hq) {
+  return (size_t)(rows / kPart + S + 1) * Hq * kState * sizeof(float);
+}
+
+hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, int rows, const void* q,
+                                   long q_stride, const void* k, long k_stride, const void* v,
+                                   long v_stride, int Hq, int Hkv, void* out, void* ws,
+                                   hipStream_t st) {
   LinAttnArgs a;
   a.cu_seqlens = cu_seqlens;
   a.q = (const uint16_t*)q;
@@ -287,12 +374,25 @@ hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, const void*
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.out = (uint16_t*)out;
-  hipError_t e = hipFuncSetAttribute((const void*)linear_attn_bf16_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e != hipSuccess) return e;
-  // heads fastest: the workgroups of one segment go out together, and a
-  // compute unit that finishes a short segment takes the next one's
-  hipLaunchKernelGGL(linear_attn_bf16_kernel, dim3(Hq, S), dim3(kThreads), kLdsBytes, st, a);
+  a.ws = (float*)ws;
+  a.S = S;
+  for (const void* f : {(const void*)linear_attn_bf16_kernel<0>,
+                        (const void*)linear_attn_bf16_kernel<1>,
+                        (const void*)linear_attn_bf16_kernel<2>}) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
+  // heads fastest: the workgroups of one segment (or part) go out together,
+  // and a compute unit that finishes a short one takes the next
+  if (!ws) {
+    hipLaunchKernelGGL(linear_attn_bf16_kernel<0>, dim3(Hq, S), dim3(kThreads), kLdsBytes, st, a);
+    return hipGetLastError();
+  }
+  const int slots = rows / kPart + S + 1;
+  hipLaunchKernelGGL(linear_attn_bf16_kernel<1>, dim3(Hq, slots), dim3(kThreads), kLdsBytes, st, a);
+  hipLaunchKernelGGL(linear_attn_prefix_kernel, dim3(Hq, S), dim3(256), 0, st, cu_seqlens, a.ws,
+                     Hq, slots);
+  hipLaunchKernelGGL(linear_attn_bf16_kernel<2>, dim3(Hq, slots), dim3(kThreads), kLdsBytes, st, a);
   return hipGetLastError();
 }
 

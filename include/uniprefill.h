@@ -307,6 +307,28 @@ up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const
                               int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
                               void* out, void* stream);
 
+/*
+ * The same layer computed chunk-parallel (the recurrence above is linear in
+ * (S, z), so a segment's running sums can be formed per part and summed):
+ * every segment is cut into parts of 1024 rows; the parts' own sums are
+ * computed in parallel, summed in part order per segment and head, and
+ * every part's outputs then computed in parallel from the sums of the parts
+ * before it.  Same results up to the order of float32 additions; the
+ * sequential depth is one part instead of the whole segment.  rows: rows of
+ * q, k, v and out (cu_seqlens[num_seqs] <= rows is a device precondition;
+ * rows / 1024 + num_seqs + 1 <= 65535).  workspace: device scratch of
+ * up_linear_attn_workspace_bytes(rows, num_seqs, Hq) bytes (66 KB per
+ * query head and part slot), 16-byte aligned, owned by the caller; its
+ * contents on entry do not matter.  Other arguments and errors as for
+ * up_linear_attn_bf16; a short workspace returns UP_ERR_WORKSPACE.
+ */
+size_t up_linear_attn_workspace_bytes(int32_t rows, int32_t num_seqs, int32_t Hq);
+up_status up_linear_attn_bf16_parts(const int32_t* cu_seqlens, int32_t num_seqs, int32_t rows,
+                                    const void* q, int64_t q_stride, const void* k,
+                                    int64_t k_stride, const void* v, int64_t v_stride, int32_t Hq,
+                                    int32_t Hkv, int32_t head_dim, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #define UP_ACT_NONE 0
 #define UP_ACT_SWIGLU 1
 up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap,

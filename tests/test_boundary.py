@@ -213,6 +213,25 @@ def test_linear_attention_argument_validation(L):
     assert la(out=ctypes.c_void_p(0x1001)) == UP_ERR_INVALID
 
 
+def test_linear_attention_parts_validation(L):
+    need = L.up_linear_attn_workspace_bytes(5000, 3, 32)
+    # slots 5000 // 1024 + 3 + 1 = 8, each 32 heads x (128 x 128 + 128) floats
+    assert need == 8 * 32 * (128 * 128 + 128) * 4
+    assert L.up_linear_attn_workspace_bytes(-1, 3, 32) == 0
+
+    def lp(rows=5000, ws=FAKE, wsb=need, S=3, D=128, cu=FAKE):
+        return L.up_linear_attn_bf16_parts(cu, S, rows, FAKE, 4096, FAKE, 1024, FAKE, 1024, 32, 8,
+                                           D, FAKE, ws, wsb, None)
+
+    assert lp(ws=None) == UP_ERR_INVALID
+    assert lp(ws=ctypes.c_void_p(0x1008)) == UP_ERR_INVALID  # not 16-byte aligned
+    assert lp(wsb=need - 1) == UP_ERR_WORKSPACE
+    assert lp(rows=-1) == UP_ERR_INVALID
+    assert lp(rows=1 << 26) == UP_ERR_UNSUPPORTED  # more part slots than one grid dimension
+    assert lp(cu=None) == UP_ERR_INVALID  # shared checks of up_linear_attn_bf16
+    assert lp(D=64) == UP_ERR_UNSUPPORTED
+
+
 def test_kept_cache_slots_validation(L):
     b = _batch()
     bp = ctypes.byref(b)
