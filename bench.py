@@ -483,6 +483,9 @@ def run_propagation(args):
             ("gate_up_swiglu", H, 2 * MLP), ("down", MLP, H)]
     stream = torch.cuda.current_stream()
     cu_all = pc.batch.cu_seqlens
+    # chunk-parallel linear attention: its workspace, allocated once
+    la_ws = torch.empty(B.up_linear_attn_workspace_bytes(T, len(call.segments), wl.Hq),
+                        dtype=torch.uint8, device="cuda")
 
     def layer(x, rows_dev, cu, ev=None):
         args_ = [(x, w_qkv, qkv, B.UP_ACT_NONE), None, (attn.view(T, H), w_o, o, B.UP_ACT_NONE),
@@ -491,7 +494,7 @@ def run_propagation(args):
             if ev is not None:
                 ev[j][0].record(stream)
             if a_ is None:
-                B.up_linear_attn_bf16(cu, q_v, k_v, v_v, attn)
+                B.up_linear_attn_bf16(cu, q_v, k_v, v_v, attn, workspace=la_ws)
             else:
                 inp, w, out, act = a_
                 B.up_linear_bf16(inp, w, out, rows_in_use=rows_dev, act=act)
@@ -538,7 +541,7 @@ def run_propagation(args):
         "value": wall_kept, "unit": "ms", "higher_is_better": False, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "one Llama-3.1-8B-shaped later linear-attention layer (4096 -> 6144, "
-                               "causal linear attention 32/8 heads x 128, 4096 -> 4096, SwiGLU "
+                               "causal linear attention 32/8 heads x 128 in parts of 1024 rows, 4096 -> 4096, SwiGLU "
                                "4096 -> 2 x 14336, 14336 -> 4096) on the packed prefill of "
                                f"{T} tokens, {kept} kept by top-p {pc.p} (block 64)",
                    "rows_all": T, "rows_kept": kept},

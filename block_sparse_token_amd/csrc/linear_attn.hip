@@ -333,22 +333,30 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
   }
 }
 
-// pass 2: per (query head, segment), the part sums of parts 0..np-2 become
-// running sums (inclusive), in part order; slots at or past `slots` (a
-// batch that breaks cu_seqlens[S] <= rows) are left alone
+// pass 2: per (query head, segment, block of 256 state elements), the part
+// sums of parts 0..np-2 become running sums (inclusive), in part order,
+// eight parts' values loaded ahead of their stores; slots at or past
+// `slots` (a batch that breaks cu_seqlens[S] <= rows) are left alone
 __global__ __launch_bounds__(256) void linear_attn_prefix_kernel(const int32_t* __restrict__ cu,
-                                                                 float* ws, int Hq, int slots) {
-  const int h = blockIdx.x, s = blockIdx.y;
+                                                                 float* __restrict__ ws, int Hq,
+                                                                 int slots) {
+  const int h = blockIdx.x, s = blockIdx.y, e = blockIdx.z * 256 + threadIdx.x;
   const int a0 = cu[s], n = cu[s + 1] - a0;
   const int np = (n + kPart - 1) / kPart;
   const long first = part_slot(cu, s);
-  if (np < 3 || first < 0 || first + np - 2 >= slots) return;
-  for (int e = threadIdx.x; e < kState; e += 256) {
-    float r = 0.f;
-    for (int q = 0; q < np - 1; ++q) {
-      float* x = ws + ((first + q) * Hq + h) * kState + e;
-      r += *x;
-      *x = r;
+  if (np < 3 || first < 0 || first + np - 2 >= slots || e >= kState) return;
+  const long step = (long)Hq * kState;
+  float* x = ws + (first * Hq + h) * kState + e;
+  float r = 0.f;
+  const int m = np - 1;
+  for (int q0 = 0; q0 < m; q0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = q0 + j < m ? x[(q0 + j) * step] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      r += v[j];
+      if (q0 + j < m) x[(q0 + j) * step] = r;
     }
   }
 }
@@ -390,8 +398,8 @@ hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, int rows, c
   }
   const int slots = rows / kPart + S + 1;
   hipLaunchKernelGGL(linear_attn_bf16_kernel<1>, dim3(Hq, slots), dim3(kThreads), kLdsBytes, st, a);
-  hipLaunchKernelGGL(linear_attn_prefix_kernel, dim3(Hq, S), dim3(256), 0, st, cu_seqlens, a.ws,
-                     Hq, slots);
+  hipLaunchKernelGGL(linear_attn_prefix_kernel, dim3(Hq, S, (kState + 255) / 256), dim3(256), 0,
+                     st, cu_seqlens, a.ws, Hq, slots);
   hipLaunchKernelGGL(linear_attn_bf16_kernel<2>, dim3(Hq, slots), dim3(kThreads), kLdsBytes, st, a);
   return hipGetLastError();
 }
