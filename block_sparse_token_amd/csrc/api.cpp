@@ -118,6 +118,28 @@ int positions_per_tile(up_dtype dt, int D, int G) {
 
 }  // namespace
 
+namespace {
+up_status check_linear_attn(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
+                            int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                            int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                            void* out) {
+  if (!cu_seqlens || !q || !k || !v || !out)
+    return fail(UP_ERR_INVALID, "cu_seqlens, q, k, v and out must be non-NULL");
+  if (num_seqs <= 0 || num_seqs > 65535)
+    return fail(UP_ERR_INVALID, "num_seqs must be in [1, 65535] (got %d)", num_seqs);
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv)
+    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (head_dim != 128) return fail(UP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (q_stride < (int64_t)Hq * head_dim || k_stride < (int64_t)Hkv * head_dim ||
+      v_stride < (int64_t)Hkv * head_dim || (q_stride | k_stride | v_stride) % 8)
+    return fail(UP_ERR_INVALID, "row strides must hold all heads and be multiples of 8 elements");
+  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) & 15)
+    return fail(UP_ERR_INVALID, "q, k and v must be 16-byte aligned");
+  if (((uintptr_t)out) & 1) return fail(UP_ERR_INVALID, "out must be 2-byte aligned");
+  return UP_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* up_last_error(void) { return g_err.c_str(); }
@@ -155,28 +177,6 @@ up_status up_peak_copy(const void* src, void* dst, size_t bytes, void* stream) {
     return fail(UP_ERR_INVALID, "src, dst and bytes must be multiples of 16");
   return device_status(up::launch_peak_copy(src, dst, bytes, as_stream(stream)), "peak copy launch");
 }
-
-namespace {
-up_status check_linear_attn(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
-                            int64_t q_stride, const void* k, int64_t k_stride, const void* v,
-                            int64_t v_stride, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                            void* out) {
-  if (!cu_seqlens || !q || !k || !v || !out)
-    return fail(UP_ERR_INVALID, "cu_seqlens, q, k, v and out must be non-NULL");
-  if (num_seqs <= 0 || num_seqs > 65535)
-    return fail(UP_ERR_INVALID, "num_seqs must be in [1, 65535] (got %d)", num_seqs);
-  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv)
-    return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
-  if (head_dim != 128) return fail(UP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
-  if (q_stride < (int64_t)Hq * head_dim || k_stride < (int64_t)Hkv * head_dim ||
-      v_stride < (int64_t)Hkv * head_dim || (q_stride | k_stride | v_stride) % 8)
-    return fail(UP_ERR_INVALID, "row strides must hold all heads and be multiples of 8 elements");
-  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) & 15)
-    return fail(UP_ERR_INVALID, "q, k and v must be 16-byte aligned");
-  if (((uintptr_t)out) & 1) return fail(UP_ERR_INVALID, "out must be 2-byte aligned");
-  return UP_OK;
-}
-}  // namespace
 
 up_status up_linear_attn_bf16(const int32_t* cu_seqlens, int32_t num_seqs, const void* q,
                               int64_t q_stride, const void* k, int64_t k_stride, const void* v,
