@@ -205,8 +205,9 @@ up_status up_linear_attn_bf16_parts(const int32_t* cu_seqlens, int32_t num_seqs,
                                    Hq, Hkv, head_dim, out);
   if (st) return st;
   if (rows < 0) return fail(UP_ERR_INVALID, "rows must be >= 0 (got %d)", rows);
-  if ((int64_t)rows / 1024 + num_seqs + 1 > 65535)
-    return fail(UP_ERR_UNSUPPORTED, "rows / 1024 + num_seqs + 1 must be <= 65535");
+  const int part = up::linear_attn_part_rows();
+  if ((int64_t)rows / part + num_seqs + 1 > 65535)
+    return fail(UP_ERR_UNSUPPORTED, "rows / %d + num_seqs + 1 must be <= 65535", part);
   if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
   if (((uintptr_t)workspace) & 15) return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
   const size_t need = up::linear_attn_workspace_bytes(rows, num_seqs, Hq);

@@ -104,6 +104,7 @@ hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_
 // ws NULL: one workgroup per (query head, segment); else the
 // chunk-parallel form over parts, ws of linear_attn_workspace_bytes(rows,
 // S, Hq) bytes
+int linear_attn_part_rows();
 size_t linear_attn_workspace_bytes(int rows, int S, int Hq);
 hipError_t launch_linear_attn_bf16(const int32_t* cu_seqlens, int S, int rows, const void* q,
                                    long q_stride, const void* k, long k_stride, const void* v,

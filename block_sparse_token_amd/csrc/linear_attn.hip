@@ -363,6 +363,8 @@ __global__ __launch_bounds__(256) void linear_attn_prefix_kernel(const int32_t* 
 
 }  // namespace
 
+int linear_attn_part_rows() { return kPart; }
+
 size_t linear_attn_workspace_bytes(int rows, int S, int Hq) {
   return (size_t)(rows / kPart + S + 1) * Hq * kState * sizeof(float);
 }
