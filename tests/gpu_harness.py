@@ -1,15 +1,6 @@
 """GPU-side test helpers: stage a generated workload on the device, run the
-library through its binding, and compare with the oracle.
-
-Tolerances (element-wise):
-  * float32 path: |gpu - oracle| <= 1e-5 * max(|oracle|, rms(oracle)) for
-    attention outputs and scores (relative 1e-5, with the tensor's rms as the
-    floor so elements near zero are not held to an impossible relative bound);
-  * bf16 path: |gpu - oracle| <= 2e-2 for attention outputs, <= 1e-3 for
-    normalised scores;
-  * selection and compaction: bit-exact, with the oracle's selection run on
-    the scores the GPU emitted.
-"""
+library through its binding, and compare with the oracle.  The element-wise
+checks and their tolerances live in ``parity_checks`` (NumPy only)."""
 from __future__ import annotations
 
 import sys
@@ -24,9 +15,8 @@ from workloads import device as WD
 from block_sparse_token_amd import binding as B
 from block_sparse_token_amd import step as ST
 
-F32_REL = 1e-5
-BF16_OUT_ABS = 2e-2
-BF16_SCORE_ABS = 1e-3
+from parity_checks import (BF16_OUT_ABS, BF16_SCORE_ABS, F32_REL, check_bf16_values,  # noqa: F401
+                           check_out, check_scores, sample_rows)
 
 
 def log(msg):
@@ -49,6 +39,35 @@ def read_back_cache(wl, kc, vc, pid, c):
     lp = torch.arange(c, device=kc.device)
     page, off = pg[lp // W.PAGE_SIZE], lp % W.PAGE_SIZE
     return ST.tensor_to_stored(kc[page, :, off, :]), ST.tensor_to_stored(vc[page, :, off, :])
+
+
+def assert_cache_unchanged_outside(before, after, slot_mapping):
+    """Every cache row [page, :, offset, :] outside ``slot_mapping`` is
+    bit-identical before and after a call (nothing wrote a wrong slot)."""
+    sm = torch.from_numpy(np.asarray(slot_mapping, np.int64)).to(after.device)
+    sm = sm[sm >= 0]
+    page, off = sm // W.PAGE_SIZE, sm % W.PAGE_SIZE
+    before[page, :, off, :] = after[page, :, off, :]
+    same = torch.equal(before, after)
+    assert same, "cache rows outside the call's slots changed"
+
+
+def check_written_slots(wl, call, kc, vc, tokens):
+    """The cache rows at the given tokens' slots hold the rotated key (bf16
+    bound against the oracle's rotation) and the value (bit-exact)."""
+    tokens = np.asarray(sorted(int(t) for t in tokens), np.int64)
+    sm = call.slot_mapping[tokens].astype(np.int64)
+    page = torch.from_numpy(sm // W.PAGE_SIZE).to(kc.device)
+    off = torch.from_numpy(sm % W.PAGE_SIZE).to(kc.device)
+    k_got = ST.tensor_to_stored(kc[page, :, off, :])
+    v_got = ST.tensor_to_stored(vc[page, :, off, :])
+    pos = call.positions[tokens].astype(np.int64)
+    k_ref = oracle.apply_rope(W.to_f64(call.k[tokens], wl.dtype), pos, wl.theta)
+    if wl.dtype == "bf16":
+        check_bf16_values(W.to_f64(k_got, "bf16"), k_ref, "cache K at the call's slots")
+    else:
+        check_out("f32", k_got, k_ref, "cache K at the call's slots")
+    assert np.array_equal(v_got, call.v[tokens]), "cache V at the call's slots"
 
 
 def row_sources(call, device="cuda"):
@@ -90,36 +109,6 @@ def gpu_result(pc):
             r["cu_seqlens_out"] = pc.cu_seqlens_out.cpu().numpy()
             r["rows_out"] = {n: ST.tensor_to_stored(t[:nk]) for n, t in pc.rows_out.items()}
     return r
-
-
-def check_out(dtype, got_stored, ref, what="out"):
-    got = W.to_f64(got_stored, dtype)
-    assert got.shape == ref.shape, (what, got.shape, ref.shape)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    err = np.abs(got - ref)
-    if dtype == "bf16":
-        worst = float(err.max()) if err.size else 0.0
-        assert worst <= BF16_OUT_ABS, f"{what}: max abs err {worst:.3e} > {BF16_OUT_ABS}"
-        return worst
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    bound = F32_REL * np.maximum(np.abs(ref), rms)
-    bad = err > bound
-    assert not bad.any(), (f"{what}: {int(bad.sum())} elements beyond relative 1e-5; worst "
-                           f"ratio {float((err / np.maximum(bound, 1e-300)).max()):.3f}")
-    return float((err / np.maximum(bound, 1e-300)).max())
-
-
-def check_scores(dtype, got, ref32):
-    ref = ref32.astype(np.float64)
-    g = got.astype(np.float64)
-    err = np.abs(g - ref)
-    if dtype == "bf16":
-        assert err.max() <= BF16_SCORE_ABS, f"scores: max abs err {err.max():.3e}"
-    else:
-        rms = float(np.sqrt(np.mean(ref * ref)))
-        bound = F32_REL * np.maximum(np.abs(ref), rms)
-        assert np.all(err <= bound), f"scores: worst ratio {float((err / bound).max()):.3f}"
-    assert np.all(g >= 0)
 
 
 def check_selection_and_compaction(wl, call, g, whole_prompt=False):
