@@ -29,7 +29,8 @@ up_status device_status(hipError_t e, const char* what) {
   return fail(UP_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool valid_block_size(int b) { return b == 16 || b == 32 || b == 64 || b == 128; }
+bool valid_block_size(int b) { return b >= 16 && b <= up::kMaxBlockSize && b % 16 == 0; }
+#define BLOCK_SIZE_RULE "block_size must be a multiple of 16 in [16, 256] (got %d)"
 
 up_status check_batch(const up_batch* b, bool need_positions) {
   if (!b) return fail(UP_ERR_INVALID, "batch is NULL");
@@ -250,7 +251,7 @@ up_status up_block_offsets(const up_batch* batch, int32_t block_size, const uint
   st = check_scope(batch, score_scope);
   if (st) return st;
   if (!valid_block_size(block_size))
-    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
   if (!cu_blocks) return fail(UP_ERR_INVALID, "cu_blocks is NULL");
   return device_status(up::launch_block_offsets(batch->cu_seqlens,
                                                 block_origin(batch, score_flags, score_scope),
@@ -268,7 +269,7 @@ size_t score_runs(const up_batch* b, int block_size, int scope) {
       scope == UP_SCOPE_PROMPT ? (size_t)b->num_seqs * b->max_pages * up::kPageSize : 0;
   const size_t nb_cap =
       ((size_t)b->num_tokens + cached + block_size - 1) / block_size + b->num_seqs;
-  return nb_cap * (size_t)(block_size / (block_size < 64 ? block_size : 64));
+  return nb_cap * (size_t)(block_size / up::score_run_len(block_size));
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
@@ -312,13 +313,18 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   if (D != 64 && D != 128) return fail(UP_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", D);
   if (!q || !k || !v || !k_cache || !v_cache || !out)
     return fail(UP_ERR_INVALID, "q, k, v, k_cache, v_cache and out must be non-NULL");
+  // rows move as 16-byte chunks (global-to-LDS copies, vector loads and stores)
+  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)k_cache) |
+       ((uintptr_t)v_cache) | ((uintptr_t)out)) & 15)
+    return fail(UP_ERR_INVALID, "q, k, v, k_cache, v_cache and out must be 16-byte aligned");
+  if (((uintptr_t)lse) & 3) return fail(UP_ERR_INVALID, "lse must be 4-byte aligned");
   if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
   if (((uintptr_t)workspace) & 15) return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
   if (!(rope_theta == rope_theta) || !(sm_scale == sm_scale))
     return fail(UP_ERR_INVALID, "rope_theta and sm_scale must not be NaN");
   if (score_flags) {
     if (!valid_block_size(block_size))
-      return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+      return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
     if (!cu_blocks || !block_mass)
       return fail(UP_ERR_INVALID, "scoring needs cu_blocks and block_mass");
   }
@@ -427,7 +433,7 @@ up_status up_block_scores(const up_batch* batch, int32_t Hq, int32_t block_size,
   if (st) return st;
   if (Hq <= 0) return fail(UP_ERR_INVALID, "Hq must be >= 1");
   if (!valid_block_size(block_size))
-    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
   if (!cu_blocks || !scores) return fail(UP_ERR_INVALID, "cu_blocks and scores must be non-NULL");
   if (score_flags && !block_mass) return fail(UP_ERR_INVALID, "block_mass is NULL");
   return device_status(up::launch_block_scores(batch->cu_seqlens, cu_blocks, score_flags,
@@ -442,7 +448,7 @@ up_status up_topp_select(const up_batch* batch, int32_t block_size, const int32_
   up_status st = check_batch(batch, false);
   if (st) return st;
   if (!valid_block_size(block_size))
-    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
   if (!(p >= 0.0 && p <= 1.0)) return fail(UP_ERR_INVALID, "p must be in [0, 1] (got %g)", p);
   if (!cu_blocks || !keep) return fail(UP_ERR_INVALID, "cu_blocks and keep must be non-NULL");
   if (score_flags && !scores) return fail(UP_ERR_INVALID, "scores is NULL");
@@ -469,7 +475,7 @@ up_status up_compact(const up_batch* batch, int32_t block_size, const int32_t* c
   st = check_scope(batch, score_scope);
   if (st) return st;
   if (!valid_block_size(block_size))
-    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
   if (!cu_blocks || !keep || !index_map || !cu_seqlens_out || !num_kept)
     return fail(UP_ERR_INVALID, "cu_blocks, keep, index_map, cu_seqlens_out, num_kept must be non-NULL");
   if (num_blocks < batch->num_seqs)
@@ -512,7 +518,7 @@ up_status up_kept_cache_slots(const up_batch* batch, int32_t block_size, const i
   st = check_scope(batch, UP_SCOPE_PROMPT);
   if (st) return st;
   if (!valid_block_size(block_size))
-    return fail(UP_ERR_UNSUPPORTED, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
   if (!cu_blocks || !score_flags || !keep || !slots || !cu_slots_out || !num_slots)
     return fail(UP_ERR_INVALID,
                 "cu_blocks, score_flags, keep, slots, cu_slots_out and num_slots must be non-NULL");

@@ -33,7 +33,8 @@
 //    is raised (and O, l rescaled) when a tile's max is 2^8 above it.
 //  * Block importance of a scored segment: the items holding the rows of
 //    its last block store, per row and head, the log2-sum-exp of every run
-//    of min(block, 64) own keys and the row's total log2-sum-exp (key tiles
+//    of 64, 32 or 16 own keys (the largest dividing the block) and the row's
+//    total log2-sum-exp (key tiles
 //    are aligned to the segment's first own key, so runs never straddle a
 //    tile); block_mass_kernel (mass.hip) then sums exp2(run - total) over
 //    the rows and runs of each block in a fixed order (deterministic).
@@ -472,7 +473,8 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
 
   // Block importance (scored segments): the rows of the segment's last
   // block store, per row and head, the log2-sum-exp of each run of Qs own
-  // keys (Qs = min(block, 64)) and their total log2-sum-exp; mass of block
+  // keys (Qs = 64, 32 or 16, the largest dividing the block) and their
+  // total log2-sum-exp; mass of block
   // b = sum over those rows of exp2(run - total) over b's runs
   // (block_mass_kernel).
   const int Bs = a.block_size;
@@ -481,7 +483,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const int r0s = scored ? (nbs - 1) * Bs : 0;
   const bool item_scores = scored && i_last >= r0s;       // same in every lane
   const bool row_scores = item_scores && rvalid && i >= r0s && h == 0;
-  const int Qs = scored ? min(Bs, C::BN) : C::BN;
+  const int Qs = scored ? score_run_len(Bs) : C::BN;
   const int run_base = scored ? a.cu_blocks[s] * (Bs / Qs) : 0;
   // first key of the scored blocks: the segment's first own key, or key 0
   // when the whole prompt is scored (cached length a multiple of the block)

@@ -175,7 +175,8 @@ __device__ void score_item_f(const AttnArgs& a, int s, int g, char* lds) {
   const float* sK = (const float*)(lds + CfgF<D>::K_OFF);
   const int* sP = (const int*)(lds + CfgF<D>::POS_OFF);
   float* red = (float*)(lds + CfgF<D>::RED_OFF);
-  const int nbt = B >= BN ? 1 : BN / B;  // blocks per key tile (<= 2)
+  // a tile of BN = 32 own keys aligned to the segment start meets at most
+  // two blocks (block sizes are multiples of 16)
   for (int ps = passes - 1; ps >= 0; --ps) {
     const int rbeg = ps * NT, rend = min(rows_total, rbeg + NT);
     const int r = rbeg + threadIdx.x;
@@ -223,21 +224,25 @@ __device__ void score_item_f(const AttnArgs& a, int s, int g, char* lds) {
           for (int d = 0; d < D; ++d) dot = fmaf(q[d], sK[kk * D + d], dot);
           dot *= a.scale;
           const float p = expf(dot - m) * inv;
-          const int bt = B >= BN ? 0 : kk / B;
+          const int bt = (mt * BN + kk) / B - (mt * BN) / B;
           if (bt == 0) part[0] += p; else part[1] += p;
         }
       }
       red[threadIdx.x * 2 + 0] = part[0];
       red[threadIdx.x * 2 + 1] = part[1];
       __syncthreads();
-      if ((int)threadIdx.x < nbt * G) {
+      if ((int)threadIdx.x < 2 * G) {
         const int bt = threadIdx.x / G, h2 = threadIdx.x % G;
         float tot = 0.f;
         for (int t = h2; t < NT; t += G) tot += red[t * 2 + bt];  // fixed order
         const int kb = (mt * BN) / B + bt;
-        if (kb < nb) {
+        // the block's keys in this tile (bt = 1 only if a block starts inside it)
+        const bool here = bt == 0 || kb * B < min((mt + 1) * BN, own_end);
+        if (kb < nb && here) {
           float* dst = a.block_mass + (mbase + kb) * a.Hq + g * G + h2;
-          const bool first = (ps == passes - 1) && (B <= BN || ((mt * BN) % B) == 0);
+          // first contribution: the pass processed first, the tile holding
+          // the block's first key
+          const bool first = (ps == passes - 1) && kb * B >= mt * BN;
           if (first) *dst = tot;
           else *dst += tot;
         }

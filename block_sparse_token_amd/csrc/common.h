@@ -12,6 +12,14 @@ namespace up {
 constexpr int kPageSize = 16;
 constexpr int kMaxSeqsPlan = 4096;  // segments per call the work planner handles
 constexpr int kMaxRopePairs = 64;   // D / 2 for D = 128
+constexpr int kMaxBlockSize = 256;  // block sizes: multiples of 16 in [16, 256]
+
+// The bf16 attention sweep records the log2-sum-exp of every run of this
+// many consecutive scored keys (a run never straddles a 64-key tile, and a
+// block is a whole number of runs).
+__host__ __device__ inline int score_run_len(int block_size) {
+  return (block_size % 64) == 0 ? 64 : (block_size % 32) == 0 ? 32 : 16;
+}
 
 // ---------------------------------------------------------------- work items
 // One attention work item = (segment, query tile) or a score item for a

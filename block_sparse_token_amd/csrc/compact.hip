@@ -58,17 +58,22 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(
     int off = carry;
     for (int w = 0; w < wid; ++w) off += wsum[w];
     const int excl = off + x - v;
-    if (k < NB) {
-      block_out[k] = excl;
-      if (k == cu_blocks[s]) cu_out[s] = excl;
-    }
+    if (k < NB) block_out[k] = excl;
     __syncthreads();
     if (tid == 1023) carry = off + x;
     __syncthreads();
   }
+  // every segment's output offset, also for a segment without blocks (it
+  // starts where the next block's rows go, or at the total); the barrier
+  // above orders these reads after the workgroup's block_out writes
+  const int total = carry;
+  for (int s = tid; s < S; s += 1024) {
+    const int k = cu_blocks[s];
+    cu_out[s] = k < NB ? block_out[k] : total;
+  }
   if (tid == 0) {
-    cu_out[S] = carry;
-    *num_kept = carry;
+    cu_out[S] = total;
+    *num_kept = total;
   }
 }
 

@@ -4,7 +4,8 @@
 // (Top-p Token Selection) and "Method & Key Results": importance per token
 // block; the pages give no formula, the reading used is this mass).  The
 // attention items store, per last-block row and head, the log2-sum-exp of
-// every run of min(block, 64) own keys and the row's total; the mass of
+// every run of 64, 32 or 16 own keys (the largest dividing the block) and
+// the row's total; the mass of
 // block b is the sum over rows of exp2(run - total) over b's runs.
 #include "common.h"
 
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restri
                                                          const float* __restrict__ score_part,
                                                          const float* __restrict__ score_lse,
                                                          int Hq, int B, float* __restrict__ mass) {
-  __shared__ float tot[128 * 32];
+  __shared__ float tot[kMaxBlockSize * 32];
   __shared__ float red[8 * 32];
   const int s = blockIdx.x;
   if (!score_flags[s]) return;
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(256) void block_mass_kernel(const int32_t* __restri
   const int nb = (off + n + B - 1) / B;
   if ((int)blockIdx.y >= nb) return;
   const int r0 = ((n + B - 1) / B - 1) * B, rows = n - r0;
-  const int Q = min(B, 64), rpb = B / Q;
+  const int Q = score_run_len(B), rpb = B / Q;
   const long run_base = (long)cu_blocks[s] * rpb;
   const int tid = threadIdx.x, rg = tid >> 5, hl = tid & 31;
   for (int hc = 0; hc < Hq; hc += 32) {

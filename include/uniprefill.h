@@ -81,7 +81,8 @@ const char* up_version(void);
  * slot_mapping[t] = page * page_size + offset.
  */
 typedef struct up_batch {
-  int32_t num_seqs;             /* (host) S >= 1                                        */
+  int32_t num_seqs;             /* (host) S >= 1; every segment holds >= 1 token (a
+                                   device precondition, checked by up_check_batch)     */
   int32_t num_tokens;           /* (host) T: row capacity of the packed arrays; the
                                    tokens in use are cu_seqlens[S] <= T (device value)   */
   const int32_t* cu_seqlens;    /* [S+1], cu_seqlens[0] = 0                              */
@@ -116,7 +117,8 @@ typedef struct up_batch {
  * block_size), cu_blocks[0] = 0, where o_s = ctx_lens[s] for a scored
  * segment (score_flags[s] != 0) under UP_SCOPE_PROMPT and 0 otherwise;
  * blocks are counted from that start (the last one may be short).
- * cu_blocks: [S+1] int32 output.  block_size: 16, 32, 64 or 128.
+ * cu_blocks: [S+1] int32 output.  block_size: a multiple of 16 in [16, 256]
+ * (UP_ERR_UNSUPPORTED otherwise), the same value in every call of one step.
  * score_flags may be NULL (no segment scored).
  */
 up_status up_block_offsets(const up_batch* batch, int32_t block_size, const uint8_t* score_flags,
@@ -136,6 +138,15 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
 
 /*
  * Attention with rotary positions, KV-cache write and fused block mass.
+ *
+ * Defined by: Ultralytics glossary "Chunked Prefill", "How chunked prefill
+ * works" (a chunk attends the cached keys and values of the earlier chunks
+ * plus its own tokens, causally over absolute positions, and the result
+ * equals one pass) and "Related serving techniques" (KV in fixed-size
+ * pages); Prepacking summary, "Technical framework" (packed prompts with a
+ * block-diagonal mask and positions restarting per prompt); UniPrefill
+ * review, "Method & Key Results" (block importance estimated at a
+ * full-attention layer inside the prefill, hence the fused block mass).
  *
  * Computes, for every token t of every segment s and every query head h
  * (KV head g = h / (Hq / Hkv)):
@@ -176,6 +187,8 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
  * out [T, Hq, D] (dtype); lse [T, Hq] f32 natural-log normaliser of each
  *        row's scaled logits, or NULL.
  * workspace: at least up_attn_workspace_bytes(...) bytes, 16-byte aligned.
+ * q, k, v, k_cache, v_cache and out must be 16-byte aligned and lse 4-byte
+ * aligned (UP_ERR_INVALID otherwise): rows move as 16-byte chunks.
  */
 up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
                           int32_t D, const void* q, const void* k, const void* v, void* k_cache,
@@ -185,7 +198,12 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Block scores: for a flagged segment s, score[b] = m_b / sum_b' m_b' with
+ * Block scores (UniPrefill review, "Method & Key Results": an importance per
+ * token block, estimated at a full-attention layer; "Key Terms &
+ * Definitions", Top-p Token Selection: importances normalised so that
+ * their cumulative sum can be compared with p).  No page gives a formula;
+ * this library's reading is the normalised block mass.
+ * For a flagged segment s, score[b] = m_b / sum_b' m_b' with
  * m_b = sum_h block_mass[b, h] (the importance of each own block,
  * normalised over the segment).  Unflagged segments get score 0 for every
  * block.  scores [NB] f32.

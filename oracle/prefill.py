@@ -12,11 +12,12 @@ call does to a packed batch of prompt segments:
   (Prepacking summary, "Technical framework" and "Key design": the attention
   mask and the positional encoding are modified so several prompts share one
   sequence);
-* chunked prefill: a segment that continues a prompt attends to the cached
-  keys and values of all earlier chunks plus its own tokens under a causal
-  mask over absolute positions, which equals a one-pass prefill
+* chunked prefill: when a prompt is fed in pieces, each piece's queries see
+  the prompt's KV record left by the pieces before it together with the
+  piece's own keys, masked by position so no query sees a later token; the
+  pieces' outputs then coincide with a single pass over the whole prompt
   (Ultralytics glossary "Chunked Prefill", section "How chunked prefill
-  works" and its code example);
+  works");
 * token importance per block and top-p block selection: the input is split
   into token blocks, each block gets an importance, and the fewest blocks
   whose cumulative importance reaches p are kept (UniPrefill review,
@@ -91,9 +92,10 @@ def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray
 def visible(q_pos: np.ndarray, k_pos: np.ndarray, window: int) -> np.ndarray:
     """Boolean [n, m]: key j is visible to query t.
 
-    Causal over absolute positions (the glossary's chunk mask is a lower
-    triangle shifted by the chunk start, i.e. key position <= query
-    position).  With ``window > 0`` only the last ``window`` positions are
+    A key is visible when its position does not exceed the query's (for a
+    chunk this is the lower-triangular mask moved along by the chunk's
+    offset, as the glossary's chunked-prefill section describes).  With
+    ``window > 0`` only the last ``window`` positions are
     visible: q_pos - window < k_pos <= q_pos.
     """
     qp = np.asarray(q_pos, dtype=np.int64)[:, None]

@@ -75,7 +75,10 @@ def test_attention_argument_validation(L):
     assert _attn(L, _batch(S=5, T=3)) == UP_ERR_INVALID
     assert _attn(L, _batch(S=4097, T=5000)) == UP_ERR_UNSUPPORTED  # work planner limit
     assert "4096" in L.up_last_error().decode()
-    assert _attn(L, b, flags=FAKE, block=48) == UP_ERR_UNSUPPORTED
+    # block sizes: multiples of 16 in [16, 256]
+    for bad in (0, 8, 24, 100, 272, 512):
+        assert _attn(L, b, flags=FAKE, block=bad) == UP_ERR_UNSUPPORTED, bad
+    assert b"multiple of 16" in L.up_last_error()
     assert _attn(L, b, theta=float("nan")) == UP_ERR_INVALID
     # whole-prompt scoring: bf16 only, needs a block table; unknown scopes refused
     assert _attn(L, b, flags=FAKE, scope=1, dtype=0, Hq=2, Hkv=2, D=64) == UP_ERR_UNSUPPORTED
@@ -88,6 +91,14 @@ def test_attention_argument_validation(L):
     assert need > 16
     assert _attn(L, b, ws_bytes=need - 1) == UP_ERR_WORKSPACE
     assert b"workspace" in L.up_last_error()
+    # 16-byte alignment of the row arrays
+    odd = ctypes.c_void_p(FAKE.value + 8)
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = odd
+        assert L.up_prefill_attn(ctypes.byref(b), 1, 8, 2, 128, *ptrs[:5], 0.0, 0, 0.0, None, 0,
+                                 0, None, None, ptrs[5], None, FAKE, 1 << 30, None) == UP_ERR_INVALID
+        assert b"16-byte aligned" in L.up_last_error()
     nb = _batch(with_ptrs=False)
     assert _attn(L, nb) == UP_ERR_INVALID
     assert b"NULL" in L.up_last_error()
@@ -101,14 +112,17 @@ def test_workspace_size_arithmetic(L):
     assert need == items
     assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 7, 128, 0, 0) == 0
     # scoring in bf16 adds, from a 256-byte boundary, one float per (run of
-    # min(block, 64) keys, last-block row, head) for every possible block,
-    # and one per (segment, last-block row, head)
+    # keys, last-block row, head) for every possible block, and one per
+    # (segment, last-block row, head); a run is 64, 32 or 16 keys, the
+    # largest of those dividing the block
     base = -(-items // 256) * 256
-    for B in (16, 64, 128):
-        runs = (math.ceil(70000 / B) + 16) * (B // min(B, 64))
+    run_len = {16: 16, 48: 16, 64: 64, 96: 32, 128: 64, 144: 16, 192: 64, 256: 64}
+    for B, rl in run_len.items():
+        runs = (math.ceil(70000 / B) + 16) * (B // rl)
         want = base + 4 * runs * B * 32 + 4 * 16 * B * 32
         assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, B, 0) == want, B
-    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 48, 0) == 0
+    for bad in (40, 264):
+        assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, bad, 0) == 0
     # float32 scores in its own items: no extra space
     assert (L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 16, 0)
             == L.up_attn_workspace_bytes(ctypes.byref(b), 0, 2, 2, 64, 0, 0))
@@ -248,5 +262,5 @@ def test_kept_cache_slots_validation(L):
     assert kc(nb=1) == UP_ERR_INVALID
     assert kc(cap=-1) == UP_ERR_INVALID
     assert kc(ws=8) == UP_ERR_WORKSPACE
-    assert L.up_kept_cache_slots(bp, 48, FAKE, FAKE, FAKE, 4, FAKE, 64, FAKE, FAKE, FAKE,
+    assert L.up_kept_cache_slots(bp, 40, FAKE, FAKE, FAKE, 4, FAKE, 64, FAKE, FAKE, FAKE,
                                  1 << 20, None) == UP_ERR_UNSUPPORTED

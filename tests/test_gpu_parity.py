@@ -84,6 +84,21 @@ CASES = [
          p=0.9, theta=0.0, q_mult=12.0),
     dict(lengths=[500, 90], ctxs=[64, 0], Hq=8, Hkv=2, D=64, dtype="bf16", block_size=32,
          p=0.9, theta=0.0, q_mult=40.0, window=200),
+    # block sizes that are multiples of 16 but not powers of two, and the
+    # largest (runs of 16, 32 and 64 keys; last blocks of up to 256 rows)
+    dict(lengths=[700, 100, 48], ctxs=[0, 37, 0], Hq=8, Hkv=2, D=128, dtype="bf16", block_size=48,
+         p=0.8, theta=500000.0),
+    dict(lengths=[1000, 333], ctxs=[0, 64], Hq=16, Hkv=4, D=128, dtype="bf16", block_size=96,
+         p=0.7, theta=500000.0, window=300),
+    dict(lengths=[1300, 257], ctxs=[0, 0], Hq=8, Hkv=8, D=64, dtype="bf16", block_size=256,
+         p=0.9, theta=500000.0),
+    dict(lengths=[900, 200], ctxs=[0, 100], Hq=32, Hkv=8, D=128, dtype="bf16", block_size=192,
+         p=0.6, theta=500000.0),
+    dict(lengths=[300, 81], ctxs=[0, 17], Hq=2, Hkv=2, D=64, dtype="f32", block_size=80,
+         p=0.7),
+    dict(lengths=[400, 70], ctxs=[16, 0], Hq=4, Hkv=2, D=64, dtype="f32", block_size=48,
+         p=0.5, theta=500000.0, window=90),
+    dict(lengths=[600], ctxs=[0], Hq=2, Hkv=2, D=128, dtype="f32", block_size=256, p=0.9),
 ]
 
 
@@ -124,6 +139,8 @@ def test_gpu_bin_packed_rows_with_padding_segments():
     (64, [88, 200, 64, 5], [512, 256, 0, 700], [True, True, True, False], 0.6),
     (16, [40, 1, 33], [48, 160, 0], [True, True, True], 0.5),
     (128, [300], [1024], [True], 0.7),
+    (48, [100, 30], [480, 96], [True, True], 0.6),
+    (256, [400], [512], [True], 0.8),
 ])
 def test_gpu_whole_prompt_scoring(B, lengths, ctxs, flags, p):
     """Final chunks scored over their whole prompt (cached blocks included):

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as W
 from oracle import prefill as P
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -117,23 +118,25 @@ def test_chunked_prefill_example_from_glossary_page():
     with open(os.path.join(GOLDEN, "chunked_prefill_example.json")) as f:
         g = json.load(f)
     L, C, H, D = g["prompt_len"], g["chunk"], g["heads"], g["head_dim"]
-    torch.manual_seed(g["torch_seed"])
-    q, k, v = torch.randn(3, 1, H, L, D).unbind(0)
-    to = lambda t: t[0].permute(1, 0, 2).double().numpy()  # -> [L, H, D]
-    q, k, v = to(q), to(k), to(v)
+    # the page's inputs: one seeded draw of q, k and v together (the fixture
+    # records the seed and the shape), as [L, H, D] float64
+    gen = torch.Generator().manual_seed(g["torch_seed"])
+    qkv = torch.randn((3, 1, H, L, D), generator=gen)[:, 0].permute(0, 2, 1, 3).double().numpy()
+    q, k, v = qkv
     pos = np.arange(L)
     full = _seg_run([(0, 0, L, False)], q, k, v, pos, [0, L], H, H, D, 0.0, 0,
                     oracle.KVCacheModel())["out"]
+    # the chunks come from this repository's chunk scheduler, and each call
+    # reads the cache the earlier calls left in the oracle's KV record
+    sched = W._chunk_schedule([L], C, flag=False)
     cache = oracle.KVCacheModel()
-    outs, lens = [], []
-    for s in range(0, L, C):
-        e = min(s + C, L)
-        lens.append(e - s)
-        r = _seg_run([(0, s, e - s, False)], q[s:e], k[s:e], v[s:e], pos[s:e], [0, e - s], H, H,
-                     D, 0.0, 0, cache)
-        outs.append(r["out"])
+    outs = []
+    for (seg,) in sched:
+        a, b = seg.ctx, seg.ctx + seg.n
+        outs.append(_seg_run([(0, seg.ctx, seg.n, False)], q[a:b], k[a:b], v[a:b], pos[a:b],
+                             [0, seg.n], H, H, D, 0.0, 0, cache)["out"])
     chunked = np.concatenate(outs)
-    assert lens == g["expected_chunk_lengths"]
+    assert [seg.n for (seg,) in sched] == g["expected_chunk_lengths"]
     assert np.allclose(full, chunked, atol=g["atol"], rtol=0) == g["expected_allclose"]
     # in float64 the two are equal far below the page's tolerance
     assert np.max(np.abs(full - chunked)) < 1e-12
