@@ -66,6 +66,9 @@ def lib():
                                         c_vp, c_vp, c_vp, c_size, c_vp]),
             "up_block_scores": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
+            "up_score_select": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp]),
+            "up_profile_rope_events": (c_i32, [c_vp, c_vp]),
             "up_compact_workspace_bytes": (c_size, [c_i32, c_i32]),
             "up_profile_attn_events": (c_i32, [c_vp, c_vp]),
             "up_check_batch": (c_i32, [bp, c_i32, c_vp, c_vp]),
@@ -96,7 +99,8 @@ EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspac
             "up_prefill_attn", "up_block_scores", "up_topp_select", "up_compact_workspace_bytes",
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
             "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16", "up_kept_cache_slots",
-            "up_linear_attn_workspace_bytes", "up_linear_attn_bf16_parts"]
+            "up_linear_attn_workspace_bytes", "up_linear_attn_bf16_parts", "up_score_select",
+            "up_profile_rope_events"]
 
 
 def _check(st: int, what: str):
@@ -186,6 +190,23 @@ def up_block_scores(batch: Batch, Hq, block_size, cu_blocks, score_flags, block_
                     stream=None):
     _check(lib().up_block_scores(batch.ref, Hq, block_size, _p(cu_blocks), _p(score_flags),
                                  _p(block_mass), _p(scores), _stream(stream)), "up_block_scores")
+
+
+def up_score_select(batch: Batch, Hq, block_size, cu_blocks, score_flags, p, block_mass, scores,
+                    keep, kept_blocks=None, stream=None):
+    """Block scores and top-p selection in one launch."""
+    _check(lib().up_score_select(batch.ref, Hq, block_size, _p(cu_blocks), _p(score_flags),
+                                 float(p), _p(block_mass), _p(scores), _p(keep), _p(kept_blocks),
+                                 _stream(stream)), "up_score_select")
+
+
+def up_profile_rope_events(start=None, stop=None):
+    """Record torch.cuda.Event ``start``/``stop`` around the rotary/cache-write
+    kernel of later up_prefill_attn calls on this thread; no arguments turns
+    it off."""
+    hs = ctypes.c_void_p(start.cuda_event) if start is not None else None
+    he = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+    _check(lib().up_profile_rope_events(hs, he), "up_profile_rope_events")
 
 
 def up_topp_select(batch: Batch, block_size, cu_blocks, score_flags, p, scores, keep,

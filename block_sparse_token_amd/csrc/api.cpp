@@ -13,6 +13,7 @@ namespace {
 
 thread_local std::string g_err;
 thread_local hipEvent_t g_attn_ev[2] = {nullptr, nullptr};
+thread_local hipEvent_t g_rope_ev[2] = {nullptr, nullptr};
 
 up_status fail(up_status st, const char* fmt, ...) {
   char buf[512];
@@ -164,6 +165,14 @@ up_status up_profile_attn_events(void* attn_start, void* attn_stop) {
   return UP_OK;
 }
 
+up_status up_profile_rope_events(void* rope_start, void* rope_stop) {
+  if ((rope_start == nullptr) != (rope_stop == nullptr))
+    return fail(UP_ERR_INVALID, "pass two events or none");
+  g_rope_ev[0] = reinterpret_cast<hipEvent_t>(rope_start);
+  g_rope_ev[1] = reinterpret_cast<hipEvent_t>(rope_stop);
+  return UP_OK;
+}
+
 up_status up_peak_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream) {
   if (workgroups < 1 || iters < 1)
     return fail(UP_ERR_INVALID, "workgroups and iters must be >= 1 (got %d, %d)", workgroups, iters);
@@ -264,12 +273,16 @@ namespace {
 // bf16 scoring scratch: runs of min(block, 64) keys of every block, one
 // value per last-block row and head, plus one total per last-block row and
 // head of every segment
-size_t score_runs(const up_batch* b, int block_size, int scope) {
+// Upper bound on the blocks of a call (cu_blocks[S]): every token in use
+// and, for whole-prompt scoring, every cached token the block table can
+// hold, plus one partial block per segment.
+size_t block_cap(const up_batch* b, int block_size, int scope) {
   const size_t cached =
       scope == UP_SCOPE_PROMPT ? (size_t)b->num_seqs * b->max_pages * up::kPageSize : 0;
-  const size_t nb_cap =
-      ((size_t)b->num_tokens + cached + block_size - 1) / block_size + b->num_seqs;
-  return nb_cap * (size_t)(block_size / up::score_run_len(block_size));
+  return ((size_t)b->num_tokens + cached + block_size - 1) / block_size + b->num_seqs;
+}
+size_t score_runs(const up_batch* b, int block_size, int scope) {
+  return block_cap(b, block_size, scope) * (size_t)(block_size / up::score_run_len(block_size));
 }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
@@ -327,6 +340,9 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
       return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
     if (!cu_blocks || !block_mass)
       return fail(UP_ERR_INVALID, "scoring needs cu_blocks and block_mass");
+    // one block-mass workgroup per possible block of the call
+    if (block_cap(batch, block_size, score_scope) > 0x7fffffff)
+      return fail(UP_ERR_UNSUPPORTED, "too many blocks in one call");
   }
   if (batch->num_seqs > up::kMaxSeqsPlan)
     return fail(UP_ERR_UNSUPPORTED, "at most %d segments per call (got %d)", up::kMaxSeqsPlan,
@@ -366,8 +382,17 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
   ra.Hkv = Hkv;
   ra.rope = rope;
   for (int j = 0; j < up::kMaxRopePairs; ++j) ra.rope_rev[j] = rev[j];
-  hipError_t e = up::launch_rope_kv(ra, bf16, D, s);
+  hipError_t e;
+  if (g_rope_ev[0]) {
+    e = hipEventRecord(g_rope_ev[0], s);
+    if (e != hipSuccess) return device_status(e, "profiling event record");
+  }
+  e = up::launch_rope_kv(ra, bf16, D, s);
   if (e != hipSuccess) return device_status(e, "rope/kv-write launch");
+  if (g_rope_ev[1]) {
+    e = hipEventRecord(g_rope_ev[1], s);
+    if (e != hipSuccess) return device_status(e, "profiling event record");
+  }
 
   int32_t* count = (int32_t*)workspace;
   int2* items = (int2*)((char*)workspace + 16);
@@ -420,7 +445,8 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
     if (e != hipSuccess) return device_status(e, "profiling event record");
   }
   if (bf16 && score_flags) {
-    e = up::launch_block_mass(a, batch->num_seqs, s);
+    e = up::launch_block_mass(a, batch->num_seqs, (int)block_cap(batch, block_size, score_scope),
+                              s);
     if (e != hipSuccess) return device_status(e, "block mass launch");
   }
   return UP_OK;
@@ -457,6 +483,26 @@ up_status up_topp_select(const up_batch* batch, int32_t block_size, const int32_
   return device_status(up::launch_topp(cu_blocks, score_flags, scores, keep, kept_blocks,
                                        batch->num_seqs, p_fx, keep_all, as_stream(stream)),
                        "top-p launch");
+}
+
+up_status up_score_select(const up_batch* batch, int32_t Hq, int32_t block_size,
+                          const int32_t* cu_blocks, const uint8_t* score_flags, double p,
+                          const float* block_mass, float* scores, uint8_t* keep,
+                          int32_t* kept_blocks, void* stream) {
+  up_status st = check_batch(batch, false);
+  if (st) return st;
+  if (Hq <= 0) return fail(UP_ERR_INVALID, "Hq must be >= 1");
+  if (!valid_block_size(block_size))
+    return fail(UP_ERR_UNSUPPORTED, BLOCK_SIZE_RULE, block_size);
+  if (!(p >= 0.0 && p <= 1.0)) return fail(UP_ERR_INVALID, "p must be in [0, 1] (got %g)", p);
+  if (!cu_blocks || !scores || !keep)
+    return fail(UP_ERR_INVALID, "cu_blocks, scores and keep must be non-NULL");
+  if (score_flags && !block_mass) return fail(UP_ERR_INVALID, "block_mass is NULL");
+  const uint32_t p_fx = (uint32_t)floor(ldexp(p, 22) + 0.5);
+  return device_status(up::launch_score_select(cu_blocks, score_flags, block_mass, scores, Hq,
+                                               keep, kept_blocks, batch->num_seqs, p_fx, p >= 1.0,
+                                               as_stream(stream)),
+                       "score/select launch");
 }
 
 size_t up_compact_workspace_bytes(int32_t num_seqs, int32_t num_blocks) {

@@ -106,7 +106,8 @@ hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens
                               const int32_t* block_table, const uint8_t* score_flags, int S,
                               int T, int max_pages, int num_pages, int grid, int32_t* err,
                               hipStream_t st);
-hipError_t launch_block_mass(const AttnArgs& a, int S, hipStream_t st);
+// blocks_cap: at least cu_blocks[S] (workgroups past it exit at once)
+hipError_t launch_block_mass(const AttnArgs& a, int S, int blocks_cap, hipStream_t st);
 hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 // ws NULL: one workgroup per (query head, segment); else the
@@ -133,6 +134,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, int D, int capacity, hipStream_t s
 hipError_t launch_block_scores(const int32_t* cu_seqlens, const int32_t* cu_blocks,
                                const uint8_t* flags, const float* mass, float* scores, int S,
                                int Hq, hipStream_t st);
+hipError_t launch_score_select(const int32_t* cu_blocks, const uint8_t* flags, const float* mass,
+                               float* scores, int Hq, uint8_t* keep, int32_t* kept_blocks, int S,
+                               uint32_t p_fx, int keep_all, hipStream_t st);
 hipError_t launch_topp(const int32_t* cu_blocks, const uint8_t* flags, const float* scores,
                        uint8_t* keep, int32_t* kept_blocks, int S, uint32_t p_fx, int keep_all,
                        hipStream_t st);

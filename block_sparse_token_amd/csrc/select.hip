@@ -35,11 +35,11 @@ __device__ inline float block_sum_f(float x, float* sh) {
   return r;
 }
 
-__global__ __launch_bounds__(kSelThreads) void block_scores_kernel(
-    const int32_t* __restrict__ cu_blocks, const uint8_t* __restrict__ flags,
-    const float* __restrict__ mass, float* __restrict__ scores, int Hq) {
-  __shared__ float sh[kSelThreads];
-  const int s = blockIdx.x;
+// Scores of segment s (one workgroup).
+__device__ inline void segment_scores(const int32_t* __restrict__ cu_blocks,
+                                      const uint8_t* __restrict__ flags,
+                                      const float* __restrict__ mass, float* __restrict__ scores,
+                                      int Hq, int s, float* sh) {
   const int b0 = cu_blocks[s], nb = cu_blocks[s + 1] - b0;
   if (!flags || !flags[s]) {
     for (int k = threadIdx.x; k < nb; k += kSelThreads) scores[b0 + k] = 0.f;
@@ -61,6 +61,13 @@ __global__ __launch_bounds__(kSelThreads) void block_scores_kernel(
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void block_scores_kernel(
+    const int32_t* __restrict__ cu_blocks, const uint8_t* __restrict__ flags,
+    const float* __restrict__ mass, float* __restrict__ scores, int Hq) {
+  __shared__ float sh[kSelThreads];
+  segment_scores(cu_blocks, flags, mass, scores, Hq, blockIdx.x, sh);
+}
+
 hipError_t launch_block_scores(const int32_t* cu_seqlens, const int32_t* cu_blocks,
                                const uint8_t* flags, const float* mass, float* scores, int S,
                                int Hq, hipStream_t st) {
@@ -75,19 +82,27 @@ __device__ inline uint64_t fx_score(float s) {
   return (uint64_t)((double)s * 1099511627776.0);
 }
 
-__global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __restrict__ cu_blocks,
-                                                         const uint8_t* __restrict__ flags,
-                                                         const float* __restrict__ scores,
-                                                         uint8_t* __restrict__ keep,
-                                                         int32_t* __restrict__ kept_blocks,
-                                                         uint32_t p_fx, int keep_all) {
-  __shared__ unsigned long long hq[256];
-  __shared__ unsigned long long red[kSelThreads];
-  __shared__ unsigned long long s_need, s_carry;
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_kept;
+struct ToppShared {
+  unsigned long long hq[256];
+  unsigned long long red[kSelThreads];
+  unsigned long long s_need, s_carry;
+  uint32_t s_prefix;
+  int s_kept;
+};
+
+// Keep mask of segment s (one workgroup).
+__device__ inline void segment_topp(const int32_t* __restrict__ cu_blocks,
+                                    const uint8_t* __restrict__ flags,
+                                    const float* __restrict__ scores, uint8_t* __restrict__ keep,
+                                    int32_t* __restrict__ kept_blocks, uint32_t p_fx, int keep_all,
+                                    int s, ToppShared& S) {
+  unsigned long long* hq = S.hq;
+  unsigned long long* red = S.red;
+  unsigned long long& s_need = S.s_need;
+  unsigned long long& s_carry = S.s_carry;
+  uint32_t& s_prefix = S.s_prefix;
+  int& s_kept = S.s_kept;
   const int tid = threadIdx.x;
-  const int s = blockIdx.x;
   const int b0 = cu_blocks[s], nb = cu_blocks[s + 1] - b0;
   const float* sc = scores + b0;
   uint8_t* kp = keep + b0;
@@ -224,6 +239,38 @@ __global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __rest
   if (kept_local) atomicAdd(&s_kept, kept_local);
   __syncthreads();
   if (kept_blocks && tid == 0) kept_blocks[s] = s_kept;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topp_kernel(const int32_t* __restrict__ cu_blocks,
+                                                         const uint8_t* __restrict__ flags,
+                                                         const float* __restrict__ scores,
+                                                         uint8_t* __restrict__ keep,
+                                                         int32_t* __restrict__ kept_blocks,
+                                                         uint32_t p_fx, int keep_all) {
+  __shared__ ToppShared sh;
+  segment_topp(cu_blocks, flags, scores, keep, kept_blocks, p_fx, keep_all, blockIdx.x, sh);
+}
+
+// Scores and selection of one segment in one workgroup: the scores it
+// writes are read back by the same workgroup after a barrier (a
+// workgroup-scope release and acquire, so every thread sees them).
+__global__ __launch_bounds__(kSelThreads) void score_select_kernel(
+    const int32_t* __restrict__ cu_blocks, const uint8_t* __restrict__ flags,
+    const float* __restrict__ mass, float* __restrict__ scores, int Hq,
+    uint8_t* __restrict__ keep, int32_t* __restrict__ kept_blocks, uint32_t p_fx, int keep_all) {
+  __shared__ float shf[kSelThreads];
+  __shared__ ToppShared sh;
+  segment_scores(cu_blocks, flags, mass, scores, Hq, blockIdx.x, shf);
+  __syncthreads();
+  segment_topp(cu_blocks, flags, scores, keep, kept_blocks, p_fx, keep_all, blockIdx.x, sh);
+}
+
+hipError_t launch_score_select(const int32_t* cu_blocks, const uint8_t* flags, const float* mass,
+                               float* scores, int Hq, uint8_t* keep, int32_t* kept_blocks, int S,
+                               uint32_t p_fx, int keep_all, hipStream_t st) {
+  hipLaunchKernelGGL(score_select_kernel, dim3(S), dim3(kSelThreads), 0, st, cu_blocks, flags,
+                     mass, scores, Hq, keep, kept_blocks, p_fx, keep_all);
+  return hipGetLastError();
 }
 
 hipError_t launch_topp(const int32_t* cu_blocks, const uint8_t* flags, const float* scores,

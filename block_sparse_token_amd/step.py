@@ -3,7 +3,8 @@
 ``PrefillCall`` allocates (once) every output and workspace a call needs and
 ``launch()`` issues the library's entry points in order on the current
 stream: block offsets, attention (with rotary positions, KV-cache write and
-fused block mass), block scores, top-p selection and compaction.  No
+fused block mass), block scores with top-p selection (one launch) and
+compaction.  No
 arithmetic of the method happens here; torch only provides memory.
 """
 from __future__ import annotations
@@ -114,6 +115,11 @@ class PrefillCall:
         B.up_topp_select(self.batch, self.block_size, self.cu_blocks, self.flags, self.p,
                          self.scores, self.keep, self.kept_blocks, stream)
 
+    def score_select_stage(self, stream=None):
+        """Scores and selection in one launch (same results as the two stages)."""
+        B.up_score_select(self.batch, self.Hq, self.block_size, self.cu_blocks, self.flags, self.p,
+                          self.block_mass, self.scores, self.keep, self.kept_blocks, stream)
+
     def compact_stage(self, stream=None):
         rows = [(src, self.rows_out[name]) for name, src in self.rows]
         B.up_compact(self.batch, self.block_size, self.cu_blocks, self.keep, self.num_blocks, rows,
@@ -127,7 +133,6 @@ class PrefillCall:
     def launch(self, stream=None):
         self.attention(stream)
         if self.flags is not None:
-            self.scores_stage(stream)
-            self.select_stage(stream)
+            self.score_select_stage(stream)
             if self.compact:
                 self.compact_stage(stream)

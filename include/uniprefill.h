@@ -229,6 +229,17 @@ up_status up_topp_select(const up_batch* batch, int32_t block_size, const int32_
                          const uint8_t* score_flags, double p, const float* scores,
                          uint8_t* keep, int32_t* kept_blocks, void* stream);
 
+/*
+ * Block scores and top-p selection in one launch: the same results as
+ * up_block_scores followed by up_topp_select with the same arguments (one
+ * workgroup per segment computes its scores, writes them, and selects on
+ * them), for callers that want both without the second launch.
+ */
+up_status up_score_select(const up_batch* batch, int32_t Hq, int32_t block_size,
+                          const int32_t* cu_blocks, const uint8_t* score_flags, double p,
+                          const float* block_mass, float* scores, uint8_t* keep,
+                          int32_t* kept_blocks, void* stream);
+
 /* One row tensor to compact: rows of row_bytes bytes, [T, row] -> [T_kept, row]. */
 typedef struct up_rows {
   const void* src;
@@ -362,6 +373,8 @@ up_status up_linear_bf16(const void* x, const void* w, void* y, int32_t rows_cap
  * turns it off.  The events must outlive the calls that record them.
  */
 up_status up_profile_attn_events(void* attn_start, void* attn_stop);
+/* The same for the rotary/cache-write kernel that up_prefill_attn launches first. */
+up_status up_profile_rope_events(void* rope_start, void* rope_stop);
 
 /*
  * Measurement aids (not part of the operator): what the chip sustains, to

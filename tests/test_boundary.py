@@ -147,6 +147,19 @@ def test_select_scores_compact_validation(L):
     assert L.up_topp_select(bp, 64, None, FAKE, 0.5, FAKE, FAKE, None, None) == UP_ERR_INVALID
     assert L.up_block_scores(bp, 0, 64, FAKE, FAKE, FAKE, FAKE, None) == UP_ERR_INVALID
     assert L.up_block_scores(bp, 8, 64, FAKE, FAKE, None, FAKE, None) == UP_ERR_INVALID
+    # the fused score + select entry validates like the two it replaces
+    ss = lambda **k: L.up_score_select(bp, k.get("Hq", 8), k.get("B", 64), k.get("cb", FAKE),
+                                       FAKE, k.get("p", 0.5), k.get("mass", FAKE), FAKE,
+                                       k.get("keep", FAKE), None, None)
+    assert ss(p=1.5) == UP_ERR_INVALID
+    assert ss(p=float("nan")) == UP_ERR_INVALID
+    assert ss(Hq=0) == UP_ERR_INVALID
+    assert ss(B=24) == UP_ERR_UNSUPPORTED
+    assert ss(cb=None) == UP_ERR_INVALID
+    assert ss(mass=None) == UP_ERR_INVALID
+    assert ss(keep=None) == UP_ERR_INVALID
+    assert L.up_profile_rope_events(FAKE, None) == UP_ERR_INVALID
+    assert L.up_profile_rope_events(None, None) == UP_OK
     assert L.up_block_offsets(bp, 100, None, 0, FAKE, None) == UP_ERR_UNSUPPORTED
     assert L.up_block_offsets(bp, 64, FAKE, 2, FAKE, None) == UP_ERR_INVALID  # unknown scope
     rows = (Bd.UpRows * 1)(Bd.UpRows(FAKE.value, FAKE.value, 0))

@@ -109,6 +109,18 @@ def test_gpu_fuzz_cases(idx):
     assert _run_and_check(wl)
 
 
+def test_gpu_scored_segment_after_many_one_block_segments():
+    """300 unscored one-token segments ahead of scored ones, so the block-mass
+    kernel's segment search runs with every probe of a round below the
+    block (regression: the search once excluded the unprobed candidates)."""
+    lengths = [1] * 300 + [700, 130]
+    ctxs = [int(x) for x in np.random.default_rng(9).integers(1, 200, size=300)] + [0, 64]
+    flags = [False] * 300 + [True, True]
+    wl = W.custom(seed=4300, hidden_width=16, lengths=lengths, ctxs=ctxs, flags=flags, Hq=8,
+                  Hkv=2, D=128, dtype="bf16", block_size=64, p=0.9, theta=500000.0)
+    assert _run_and_check(wl)
+
+
 def test_gpu_most_segments_per_call():
     """4096 segments (the planner's limit) of 1..9 tokens, some with cached
     prefixes, alternate segments scored."""
@@ -186,3 +198,30 @@ def test_gpu_whole_prompt_scoring(B, lengths, ctxs, flags, p):
     assert np.all(slots[n:].cpu().numpy() == -7)
     counts = [len(u) for u in pos]
     assert np.array_equal(cu_out.cpu().numpy(), np.concatenate([[0], np.cumsum(counts)]))
+
+
+def test_gpu_fused_score_select_equals_separate_stages():
+    """up_score_select gives bit for bit what up_block_scores followed by
+    up_topp_select give on the same block mass (ragged segments, unscored
+    segments, p below and at 1)."""
+    import torch
+    import gpu_harness as H
+
+    for p in (0.0, 0.6, 0.95, 1.0):
+        wl = W.custom(seed=31, hidden_width=16, lengths=[700, 1, 130, 64, 257],
+                      ctxs=[0, 40, 0, 16, 0], flags=[True, False, True, True, True], Hq=8, Hkv=2,
+                      D=128, dtype="bf16", block_size=64, p=p, theta=500000.0)
+        call = wl.calls[0]
+        kc, vc = H.make_caches(wl)
+        pc = H.launch_call(wl, call, kc, vc, compact=False)
+        fused = (pc.scores.clone(), pc.keep.clone(), pc.kept_blocks.clone())
+        pc.scores.fill_(-1.0)
+        pc.keep.fill_(7)
+        pc.kept_blocks.fill_(-1)
+        pc.scores_stage()
+        pc.select_stage()
+        torch.cuda.synchronize()
+        assert torch.equal(fused[0].view(torch.int32), pc.scores.view(torch.int32)), p
+        assert torch.equal(fused[1], pc.keep), p
+        assert torch.equal(fused[2], pc.kept_blocks), p
+        H.check_selection_and_compaction(wl, call, H.gpu_result(pc))
