@@ -1,21 +1,27 @@
-"""Benchmark: packed prefill tokens/s of one operator call on one MI355X.
+"""Benchmark: packed prefill tokens/s of the operator on one MI355X.
 
-Workload: the Llama-3.1-8B-shaped packed prefill (16 prompts, lengths
-uniform in [512, 8192] from seed 2, about 70K tokens; 32 query / 8 KV heads
-x 128, bf16; rotary base 500000; block 64, top-p 0.95; hidden width 4096).
-One step = the whole hot path on that batch: rotary embedding and paged
-KV-cache write, attention with the fused block mass, block scores, top-p
-selection and compaction of hidden states, positions and KV slots.  Inputs
-are synthetic and resident on the GPU before timing starts.
+One step = the whole hot path over one batch: rotary embedding and paged
+KV-cache write, attention with the fused block mass, block scores with top-p
+selection, and compaction of the kept rows (every call of a chunked
+workload, and the sliding-window second layer where the workload has one).
+Inputs are synthetic and resident on the GPU before timing starts.
 
-Prints one JSON line.  ``roofline`` covers the attention kernel (the
-dominant one): algorithmic flops 4 * D * Hq * (causal in-segment query/key
-pairs) per launch over its average duration, timed with HIP events recorded
-by the library around that kernel on its stream; ``attainable`` beside the
-published ``peak`` is what a plain bf16 matrix-core loop sustains on the
-same GPU in the same run (and ``attainable_peaks`` the copy rate too).
-``cpu_baseline`` is the float64 NumPy oracle timed on this host on a sample
-of the same batch.
+The default run prints one JSON line for the headline workload - the
+Llama-3.1-8B-shaped packed prefill (16 prompts, lengths uniform in
+[512, 8192] from seed 2, about 70K tokens; 32 query / 8 KV heads x 128,
+bf16; rotary base 500000; block 64, top-p 0.95; hidden width 4096) - and
+the same measurements of the four other workloads under ``configs`` (the
+tiny fp32 chunked batch, the chunked 128K prompt, the decode + prefill
+step, the selection followed by a sliding-window layer).
+
+``roofline`` covers the attention kernel (the dominant one): algorithmic
+flops 4 * D * Hq * (visible query/key pairs) per launch over its average
+duration, timed with HIP events the library records around that kernel on
+its stream; ``attainable`` beside the published ``peak`` is what a plain
+bf16 matrix-core loop sustains on the same GPU in the same run.  Every other
+pass is set against HBM with the bytes it must move (``passes``).
+``cpu_baseline`` is the float64 NumPy oracle timed on this host on a bounded
+sample of the same workload, scaled to the whole workload by visible pairs.
 """
 from __future__ import annotations
 
@@ -36,6 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 PEAK_F32_VECTOR_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "packed_llama8b"
+METRIC = "packed prefill tokens/s (attn+score+select+compact) + % MFMA/HBM roofline"
 OTHER_WORKLOADS = ("small_chunked_fp32", "chunked_128k", "mixed_decode_prefill",
                    "swa_after_selection")
 
@@ -61,15 +68,12 @@ def parse():
     ap.add_argument("--propagation", action="store_true",
                     help="time one later layer's linear maps on all vs the kept tokens of the "
                          "headline batch")
-    ap.add_argument("--workload", default=WORKLOAD, choices=(WORKLOAD,) + OTHER_WORKLOADS,
-                    help="the headline workload (default) or one of the other parity workloads, "
-                         "timed over all of its calls")
+    ap.add_argument("--workload", default="all", choices=("all", WORKLOAD) + OTHER_WORKLOADS,
+                    help="all (default): the headline workload's bench line with every other "
+                         "workload under 'configs'; or one workload, timed over all its calls")
+    ap.add_argument("--library", action="store_true",
+                    help="also time torch's flash attention on the headline batch (reference)")
     return ap.parse_args()
-
-
-def algorithmic_pairs(call):
-    """Visible (query, key) pairs: cached keys plus the causal triangle."""
-    return sum(s.n * s.ctx + s.n * (s.n + 1) // 2 for s in call.segments)
 
 
 def visible_pairs(cu, ctx, positions, window):
@@ -87,180 +91,321 @@ def visible_pairs(cu, ctx, positions, window):
     return total
 
 
-def run_other_workload(args):
-    """Time every call of a parity workload as one step (inputs resident).
-    The second layer of swa_after_selection runs on the compacted rows at
-    full row capacity (its token count stays on the device)."""
-    import torch
-    import workloads as W
-    from workloads import device as WD
-    from block_sparse_token_amd import binding as B
-    from block_sparse_token_amd import step as ST
+# ---------------------------------------------------------------------------
+# every workload: staging, timing, algorithmic work, oracle sample
+# ---------------------------------------------------------------------------
+# (name, label of the configuration it stands for, steps cap, warm-up cap)
+CONFIGS = [("packed_llama8b", "C2", None, None), ("small_chunked_fp32", "C1", 20, 3),
+           ("chunked_128k", "C3", 3, 1), ("mixed_decode_prefill", "C4", 10, 2),
+           ("swa_after_selection", "C5", 3, 1)]
+DESCRIBE = {
+    "small_chunked_fp32": "tiny packed prefill, fp32: prompts {37,100,64,255}, 2+2 heads x 64, "
+                          "block 16, top-p 0.9, chunk 64 (4 calls over the paged cache)",
+    "packed_llama8b": "Llama-3.1-8B-shaped packed prefill: 16 prompts U{512..8192} (seed 2), "
+                      "32/8 heads x 128, bf16, rope 5e5, block 64, top-p 0.95, hidden 4096",
+    "chunked_128k": "one 131072-token prompt in 16 chunks of 8192 over a paged cache, 32/8 x 128, "
+                    "bf16, rope 5e5, block 128, top-p 0.9, hidden 4096",
+    "mixed_decode_prefill": "continuous-batching step: 256 decodes (context U{1024..32768}) + "
+                            "FCFS prefill chunks to 8192 tokens, 32/8 x 128, bf16, block 64, "
+                            "top-p 0.95 on the prefill",
+    "swa_after_selection": "8 prompts U{8192..32768}: full-attention layer with scoring, block "
+                           "64, top-p 0.9, compaction of hidden/positions/slots/layer-2 q,k,v, "
+                           "then sliding-window (4096) attention on the kept tokens",
+}
 
-    wl = W.make(args.workload)
-    kc, vc = WD.make_caches(wl)
-    calls = []
-    whole = args.whole_prompt
-    if whole and args.workload != "chunked_128k":
-        raise SystemExit("--whole-prompt applies to chunked_128k (one prompt in chunks)")
-    for ci, call in enumerate(wl.calls):
-        batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions, call.slot_mapping,
-                              call.block_table)
-        final = ci == len(wl.calls) - 1
-        fl = call.flags.astype(np.uint8)
-        if whole:  # earlier chunks pass through; the final one scores the prompt
-            fl = fl * np.uint8(final)
-        flags = torch.from_numpy(fl).cuda()
-        calls.append((call, ST.PrefillCall(
-            batch=batch, q=WD.stored_to_tensor(call.q), k=WD.stored_to_tensor(call.k),
-            v=WD.stored_to_tensor(call.v), k_cache=kc, v_cache=vc,
-            num_blocks=call.num_blocks(wl.block_size, whole and final), flags=flags,
-            block_size=wl.block_size, p=wl.p, rope_theta=wl.theta, window=wl.window,
-            rows=WD.row_sources(call),
-            score_scope=B.UP_SCOPE_PROMPT if whole and final else B.UP_SCOPE_SEGMENT)))
-    layer2 = None
-    if wl.layer2:
-        pc = calls[0][1]
-        S = len(calls[0][0].segments)
-        batch2 = B.Batch(pc.cu_seqlens_out, torch.zeros(S, dtype=torch.int32, device="cuda"),
-                         pc.rows_out["positions"], pc.rows_out["slot_mapping"], None)
-        layer2 = ST.PrefillCall(batch=batch2, q=pc.rows_out["q2"], k=pc.rows_out["k2"],
-                                v=pc.rows_out["v2"], k_cache=torch.zeros_like(kc),
-                                v_cache=torch.zeros_like(vc), num_blocks=1, flags=None,
-                                block_size=wl.block_size, p=wl.p,
-                                rope_theta=wl.layer2["theta"], window=wl.layer2["window"])
+
+class Staged:
+    """A workload's calls staged on the GPU (inputs resident before timing)."""
+
+    def __init__(self, torch, wl, whole=False):
+        from workloads import device as WD
+        from block_sparse_token_amd import binding as B
+        from block_sparse_token_amd import step as ST
+
+        self.wl = wl
+        self.kc, self.vc = WD.make_caches(wl)
+        self.calls = []
+        for ci, call in enumerate(wl.calls):
+            batch = ST.make_batch(call.cu_seqlens, call.ctx_lens, call.positions,
+                                  call.slot_mapping, call.block_table)
+            final = ci == len(wl.calls) - 1
+            fl = call.flags.astype(np.uint8)
+            if whole:  # earlier chunks pass through; the final one scores the prompt
+                fl = fl * np.uint8(final)
+            self.calls.append((call, ST.PrefillCall(
+                batch=batch, q=WD.stored_to_tensor(call.q), k=WD.stored_to_tensor(call.k),
+                v=WD.stored_to_tensor(call.v), k_cache=self.kc, v_cache=self.vc,
+                num_blocks=call.num_blocks(wl.block_size, whole and final),
+                flags=torch.from_numpy(fl).cuda(), block_size=wl.block_size, p=wl.p,
+                rope_theta=wl.theta, window=wl.window, rows=WD.row_sources(call),
+                score_scope=B.UP_SCOPE_PROMPT if whole and final else B.UP_SCOPE_SEGMENT)))
+        self.layer2 = None
+        if wl.layer2:
+            # the second layer runs on the compacted rows at full row capacity
+            # (its token count stays on the device)
+            pc = self.calls[0][1]
+            S = len(self.calls[0][0].segments)
+            batch2 = B.Batch(pc.cu_seqlens_out, torch.zeros(S, dtype=torch.int32, device="cuda"),
+                             pc.rows_out["positions"], pc.rows_out["slot_mapping"], None)
+            self.layer2 = ST.PrefillCall(batch=batch2, q=pc.rows_out["q2"], k=pc.rows_out["k2"],
+                                         v=pc.rows_out["v2"], k_cache=torch.zeros_like(self.kc),
+                                         v_cache=torch.zeros_like(self.vc), num_blocks=1,
+                                         flags=None, block_size=wl.block_size, p=wl.p,
+                                         rope_theta=wl.layer2["theta"],
+                                         window=wl.layer2["window"])
+
+
+def time_workload(torch, st, steps, warmup, flush=None):
+    """Time ``steps`` steps (every call, then the second layer if any) after
+    ``warmup`` untimed ones.  Per step: wall time, and HIP-event times of the
+    rotary/cache-write kernel, the attention kernel (both recorded by the
+    library on its stream), and of each stage: the attention call (block
+    offsets, rotary/cache write, work plan, attention, block mass), scores
+    with top-p, compaction.  ``flush``: a buffer written before every step
+    (outside the timed stages) so no pass finds its inputs in the 256 MB
+    Infinity Cache."""
+    from block_sparse_token_amd import binding as B
+
     stream = torch.cuda.current_stream()
 
     def ev():
         e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)
+        e.record(stream)  # creates the event the library records again
         return e
 
     def one_step(rec):
-        for _, pc in calls:
-            e = [ev() for _ in range(5)] if rec is not None else None
-            k = (ev(), ev()) if rec is not None else None
+        for call, pc in st.calls:
             if rec is not None:
-                B.up_profile_attn_events(*k)
-                e[0].record(stream)
+                re, ae = (ev(), ev()), (ev(), ev())
+                B.up_profile_rope_events(*re)
+                B.up_profile_attn_events(*ae)
+                e = [ev()]
             pc.attention()
             if rec is not None:
-                e[1].record(stream)
-            pc.scores_stage()
+                e.append(ev())
+            if pc.flags is not None:
+                pc.score_select_stage()
             if rec is not None:
-                e[2].record(stream)
-            pc.select_stage()
+                e.append(ev())
+            if pc.flags is not None and pc.compact:
+                pc.compact_stage()
             if rec is not None:
-                e[3].record(stream)
-            pc.compact_stage()
+                e.append(ev())
+                rec.append(("call", re, ae, e))
+        if st.layer2 is not None:
             if rec is not None:
-                e[4].record(stream)
-                rec.append(("call", e, k))
-        if layer2 is not None:
-            k = (ev(), ev()) if rec is not None else None
+                re, ae = (ev(), ev()), (ev(), ev())
+                B.up_profile_rope_events(*re)
+                B.up_profile_attn_events(*ae)
+                e = [ev()]
+            st.layer2.attention()
             if rec is not None:
-                B.up_profile_attn_events(*k)
-            layer2.attention()
-            if rec is not None:
-                rec.append(("layer2", None, k))
+                e.append(ev())
+                rec.append(("layer2", re, ae, e))
         if rec is not None:
+            B.up_profile_rope_events()
             B.up_profile_attn_events()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         one_step(None)
     torch.cuda.synchronize()
-    recs = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    recs, wall = [], 0.0
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 255)
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
         one_step(recs)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    K = args.steps
-    ms_step = wall * 1e3 / K
-    attn = sum(a.elapsed_time(b) for kind, _, (a, b) in recs if kind == "call") / K
-    l2 = sum(a.elapsed_time(b) for kind, _, (a, b) in recs if kind == "layer2") / K
-    st = np.zeros(4)
-    for kind, e, _ in recs:
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+    K = float(steps)
+    t = {"ms_per_step": wall * 1e3 / K}
+    for kind in ("call", "layer2"):
+        rs = [r for r in recs if r[0] == kind]
+        if not rs:
+            continue
+        pre = "" if kind == "call" else "layer2_"
+        t[pre + "rope_ms"] = sum(a.elapsed_time(b) for _, (a, b), _, _ in rs) / K
+        t[pre + "attn_ms"] = sum(a.elapsed_time(b) for _, _, (a, b), _ in rs) / K
+        t[pre + "attn_stage_ms"] = sum(e[0].elapsed_time(e[1]) for *_, e in rs) / K
         if kind == "call":
-            st += [e[j].elapsed_time(e[j + 1]) for j in range(4)]
-    st /= K
+            t["score_select_ms"] = sum(e[1].elapsed_time(e[2]) for *_, e in rs) / K
+            t["compact_ms"] = sum(e[2].elapsed_time(e[3]) for *_, e in rs) / K
+    return t
 
-    # algorithmic work
-    e_b = 2 if wl.dtype == "bf16" else 4
-    pairs = sum(visible_pairs(c.cu_seqlens, c.ctx_lens, c.positions, wl.window) for c, _ in calls)
-    flops = 4.0 * wl.D * wl.Hq * pairs
-    T_all = sum(c.T for c, _ in calls)
-    rope_bytes = sum(c.T * (4 * wl.Hkv * wl.D * e_b + 8) for c, _ in calls)
-    kept = [int(pc.num_kept.item()) for _, pc in calls]
-    W_b = wl.hidden_width * e_b
-    # extra row tensors (read and written once per kept row)
-    extra_b = sum(2 * x[0].nbytes for x in calls[0][0].extra.values())
-    compact_bytes = sum(k * (2 * W_b + 20 + extra_b) + c.num_blocks(wl.block_size)
-                        for k, (c, _) in zip(kept, calls))
+
+def _pass(nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9 if ms > 0 else None
+    return {"bytes": int(nbytes), "us": ms * 1e3, "GB/s": gbs,
+            "frac": gbs / PEAK_HBM_GBS if gbs else None}
+
+
+def workload_metrics(st, t):
+    """Throughput, the attention pass against the matrix (or vector) peak,
+    and every other pass against HBM, from algorithmic work only: visible
+    (query, key) pairs, bytes each pass must move."""
+    wl = st.wl
     bf16 = wl.dtype == "bf16"
+    e_b = 2 if bf16 else 4
+    pairs = sum(visible_pairs(c.cu_seqlens, c.ctx_lens, c.positions, wl.window)
+                for c, _ in st.calls)
+    flops = 4.0 * wl.D * wl.Hq * pairs
+    T_all = sum(c.T for c, _ in st.calls)
+    S_all = sum(c.S for c, _ in st.calls)
+    NB_all = sum(int(pc.cu_blocks[-1].item()) for _, pc in st.calls)
+    kept = [int(pc.num_kept.item()) for _, pc in st.calls]
+    row_b = sum(src[0].numel() * src.element_size() for _, src in st.calls[0][1].rows)
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VECTOR_TFLOPS
-    achieved = flops / (attn * 1e-3) / 1e12
     tokens = T_all
-    res_extra = {}
-    if whole:
-        pc_f = calls[-1][1]
-        nbp = int(pc_f.cu_blocks[-1].item())
-        keep = pc_f.keep[:nbp].cpu().numpy().astype(bool)
-        sc = pc_f.scores[:nbp].cpu().numpy()
-        hb = -(-wl.heavy_prefix // wl.block_size)  # blocks holding the heavy-hitter cluster
-        res_extra["whole_prompt"] = {
-            "prompt_blocks": nbp, "kept_blocks": int(keep.sum()),
-            "cluster_blocks": hb, "cluster_blocks_kept": int(keep[:hb].sum()),
-            "other_blocks_kept": int(keep[hb:].sum()),
-            "mean_score_cluster": float(sc[:hb].mean()), "mean_score_other": float(sc[hb:].mean()),
-            "kept_cached_tokens": int(pc_f.num_kept_slots.item()),
-            "kept_own_tokens": int(pc_f.num_kept.item())}
-    if args.workload == "mixed_decode_prefill":
-        c = calls[0][0]
+    m = {"calls": len(st.calls), "tokens": T_all, "kept_tokens": int(sum(kept)),
+         "blocks": NB_all, "segments": S_all}
+    if wl.name == "mixed_decode_prefill":
+        c = st.calls[0][0]
         dec = [i for i, s in enumerate(c.segments) if not s.flagged]
-        tokens = int(sum(c.segments[i].n for i in range(len(c.segments)) if c.segments[i].flagged))
+        tokens = int(sum(s.n for s in c.segments if s.flagged))
         dec_keys = sum(c.segments[i].ctx + c.segments[i].n for i in dec)
         dec_bytes = dec_keys * wl.Hkv * wl.D * e_b * 2 + len(dec) * wl.Hq * wl.D * e_b * 2
         pre_pairs = pairs - sum(c.segments[i].ctx + 1 for i in dec)
-        floor_ms = dec_bytes / (PEAK_HBM_GBS * 1e9) * 1e3 + \
-            4.0 * wl.D * wl.Hq * pre_pairs / (PEAK_BF16_TFLOPS * 1e12) * 1e3
-        res_extra["decode_prefill"] = {
+        floor_ms = (dec_bytes / (PEAK_HBM_GBS * 1e9) +
+                    4.0 * wl.D * wl.Hq * pre_pairs / (PEAK_BF16_TFLOPS * 1e12)) * 1e3
+        m["decode_part"] = {
             "decode_segments": len(dec), "decode_kv_bytes": dec_bytes,
-            "prefill_pairs": pre_pairs, "serial_floor_ms": floor_ms,
-            "attention_vs_floor": floor_ms / attn, "all_tokens_per_s": T_all / (ms_step * 1e-3)}
-    if layer2 is not None:
+            "decode_kv_GB/s_if_alone": dec_bytes / (t["attn_ms"] * 1e-3) / 1e9,
+            "prefill_pairs": pre_pairs,
+            "serial_floor_ms": floor_ms, "attention_vs_serial_floor": floor_ms / t["attn_ms"],
+            "note": "the attention launch serves both parts at once; the floor is the decode KV "
+                    "read at 8 TB/s plus the prefill products at 2.5 PFLOP/s"}
+        m["all_tokens_per_s"] = T_all / (t["ms_per_step"] * 1e-3)
+    m["tokens_counted"] = tokens
+    m["ms_per_step"] = t["ms_per_step"]
+    m["tokens_per_s"] = tokens / (t["ms_per_step"] * 1e-3)
+    att = flops / (t["attn_ms"] * 1e-3) / 1e12
+    m["attention"] = {"kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
+                      "bound": "mfma" if bf16 else "alu", "pairs": pairs, "flops": flops,
+                      "ms": t["attn_ms"], "TFLOP/s": att, "peak": peak, "frac": att / peak}
+    a1_b = T_all * (4 * wl.Hkv * wl.D * e_b + 8)
+    sel_b = 4 * wl.Hq * NB_all + 4 * NB_all + 4 * NB_all + NB_all + 4 * S_all
+    comp_b = sum(k * (2 * row_b + 4) for k in kept) + NB_all
+    m["passes"] = {
+        "rope_kv_write": _pass(a1_b, t["rope_ms"]),
+        "scores_select": dict(_pass(sel_b, t["score_select_ms"]), bound="latency"),
+        "compact": _pass(comp_b, t["compact_ms"]),
+        "plan_offsets_mass_us": (t["attn_stage_ms"] - t["rope_ms"] - t["attn_ms"]) * 1e3,
+    }
+    if st.layer2 is not None:
         nk = kept[0]
-        cu2 = calls[0][1].cu_seqlens_out.cpu().numpy()
-        pos2 = calls[0][1].rows_out["positions"][:nk].cpu().numpy()
+        pc = st.calls[0][1]
+        cu2 = pc.cu_seqlens_out.cpu().numpy()
+        pos2 = pc.rows_out["positions"][:nk].cpu().numpy()
         pairs2 = visible_pairs(cu2, np.zeros(len(cu2) - 1, dtype=np.int64), pos2,
                                wl.layer2["window"])
-        flops2 = 4.0 * wl.D * wl.Hq * pairs2
-        res_extra["swa_layer"] = {"kept_tokens": nk, "pairs": pairs2, "flops": flops2,
-                                  "ms": l2, "TFLOP/s": flops2 / (l2 * 1e-3) / 1e12,
-                                  "frac": flops2 / (l2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-    rope_ms = st[0] - attn
-    res = {
-        "metric": "packed prefill tokens/s (attn+score+select+compact) + % MFMA/HBM roofline",
-        "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": args.workload, "calls": len(calls), "tokens": T_all,
-                   "tokens_counted": tokens, "kept_tokens": kept if len(kept) > 1 else kept[0]},
-        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                     "kernel": "attn_bf16_kernel" if bf16 else "attn_f32_kernel",
-                     "avg_ms": attn, "flops_per_step": flops, "pairs": pairs},
-        "stages_ms": {"rope_kv+plan": rope_ms, "attention": attn, "scores": float(st[1]),
-                      "select": float(st[2]), "compact": float(st[3]),
-                      "swa_layer": l2 if layer2 is not None else None},
-        "hbm": {"rope_kv": {"bytes": rope_bytes, "GB/s": rope_bytes / (rope_ms * 1e-3) / 1e9,
-                            "frac": rope_bytes / (rope_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-                "compact": {"bytes": compact_bytes,
-                            "GB/s": compact_bytes / (st[3] * 1e-3) / 1e9,
-                            "frac": compact_bytes / (st[3] * 1e-3) / 1e9 / PEAK_HBM_GBS}},
-    }
-    res.update(res_extra)
-    print(json.dumps(res), flush=True)
+        f2 = 4.0 * wl.D * wl.Hq * pairs2
+        a2 = f2 / (t["layer2_attn_ms"] * 1e-3) / 1e12
+        m["swa_layer"] = {"kept_tokens": nk, "window": wl.layer2["window"], "pairs": pairs2,
+                          "flops": f2, "ms": t["layer2_attn_ms"], "TFLOP/s": a2,
+                          "frac": a2 / PEAK_BF16_TFLOPS,
+                          "rope_kv_write": _pass(nk * (4 * wl.Hkv * wl.D * e_b + 8),
+                                                 t["layer2_rope_ms"])}
+    return m
+
+
+def oracle_sample(wl, budget_s, layer2_pairs=None):
+    """The float64 oracle on a bounded sample of the workload, timed on this
+    host's cores: whole segments, each in one pass (no cache needed), picked
+    as the workload allows; the whole-workload rate is the sample's rate
+    scaled by visible (query, key) pairs (its cost grows with them, and the
+    second layer's are included for the sliding-window workload)."""
+    import oracle
+    from oracle import driver
+    from oracle.prefill import default_threads
+    from workloads import to_f64
+
+    threads = default_threads()
+    dt = wl.dtype
+
+    def seg_args(call, si, extra_rows=()):
+        s = call.segments[si]
+        a, b = int(call.cu_seqlens[si]), int(call.cu_seqlens[si + 1])
+        rows = {"hidden": call.hidden[a:b], "positions": call.positions[a:b],
+                "slot_mapping": call.slot_mapping[a:b]}
+        for r in extra_rows:
+            rows[r] = call.extra[r][a:b]
+        return dict(segments=[(0, 0, s.n, s.flagged)], q=to_f64(call.q[a:b], dt),
+                    k=to_f64(call.k[a:b], dt), v=to_f64(call.v[a:b], dt),
+                    positions=call.positions[a:b], cu_seqlens=[0, s.n], Hq=wl.Hq, Hkv=wl.Hkv,
+                    D=wl.D, theta=wl.theta, window=wl.window, block_size=wl.block_size,
+                    p=wl.p, cache=oracle.KVCacheModel(), rows=rows, threads=threads)
+
+    def seg_pairs(n):
+        return n * (n + 1) // 2
+
+    total_pairs = sum(visible_pairs(c.cu_seqlens, c.ctx_lens, c.positions, wl.window)
+                      for c in wl.calls)
+    tokens = sum(c.T for c in wl.calls)
+    spent, s_tok, s_pairs, what = 0.0, 0, 0, ""
+    if wl.name == "small_chunked_fp32":
+        t0 = time.perf_counter()
+        driver.run_workload(wl, threads=threads)
+        spent = time.perf_counter() - t0
+        s_tok, s_pairs = tokens, total_pairs
+        what = "the whole workload (4 chunked calls)"
+    elif wl.layer2 is None:
+        call = wl.calls[0]
+        cand = [i for i, s in enumerate(call.segments) if s.ctx == 0 and s.flagged]
+        if wl.name == "mixed_decode_prefill":
+            c = wl.calls[0]
+            tokens = int(sum(s.n for s in c.segments if s.flagged))
+            total_pairs = sum(s.n * s.ctx + seg_pairs(s.n) for s in c.segments if s.flagged)
+        lens = np.array([call.segments[i].n for i in cand])
+        wmean = float((lens ** 2).sum() / lens.sum())
+        used = []
+        for j in np.argsort(np.abs(lens - wmean)):
+            si = cand[int(j)]
+            args = seg_args(call, si)
+            t0 = time.perf_counter()
+            oracle.run_call(**args)
+            spent += time.perf_counter() - t0
+            n = call.segments[si].n
+            s_tok += n
+            s_pairs += seg_pairs(n)
+            used.append(n)
+            if spent >= budget_s:
+                break
+        what = (f"{len(used)} whole prompt segment(s) of the first call (lengths {used}), "
+                "each in one pass")
+        if wl.name == "mixed_decode_prefill":
+            what += "; rate in prefill tokens, scaled by the prefill's pairs"
+    else:
+        call = wl.calls[0]
+        si = int(np.argmin([s.n for s in call.segments]))
+        t0 = time.perf_counter()
+        r1 = oracle.run_call(**seg_args(call, si, ("q2", "k2", "v2")))
+        ro, cu2 = r1["rows_out"], r1["cu_seqlens_out"]
+        n2 = int(cu2[-1])
+        oracle.run_call(segments=[(0, 0, n2, False)], q=to_f64(ro["q2"], dt),
+                        k=to_f64(ro["k2"], dt), v=to_f64(ro["v2"], dt),
+                        positions=ro["positions"], cu_seqlens=cu2, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                        theta=wl.layer2["theta"], window=wl.layer2["window"],
+                        block_size=wl.block_size, p=wl.p, cache=oracle.KVCacheModel(),
+                        score=False, select=False, threads=threads)
+        spent = time.perf_counter() - t0
+        n = call.segments[si].n
+        w2 = wl.layer2["window"]
+        p2 = visible_pairs(cu2, [0], ro["positions"], w2)
+        s_tok, s_pairs = n, seg_pairs(n) + p2
+        # the whole workload's second-layer pairs: from the GPU's compaction,
+        # which the parity tests hold bit-exact to the oracle's
+        total_pairs += int(layer2_pairs)
+        what = (f"the shortest prompt (length {n}) through the scored layer, compaction and "
+                f"the sliding-window layer on its {n2} kept tokens")
+    rate = s_tok / spent
+    scaled = tokens / (spent * total_pairs / s_pairs)
+    return {"value": scaled, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what}: {s_tok} tokens, {spent:.1f} s of float64 NumPy on {threads} "
+                      f"threads ({rate:.0f} tokens/s on the sample), scaled to the whole "
+                      f"workload by visible (query, key) pairs ({s_pairs} in the sample, "
+                      f"{total_pairs} in the workload)",
+            "sample_tokens_per_s": rate, "sample_seconds": spent}
 
 
 def kernel_code_hash(path):
@@ -398,42 +543,6 @@ def library_attention(torch, wl, call, pc, steps):
         return out
     except Exception as ex:  # a reference only: report, never fail the bench
         return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
-
-
-def cpu_baseline(wl, call, budget_s):
-    """Time the oracle on whole prompts of the batch, picked near the
-    token-weighted mean length (attention cost per token grows with length),
-    adding prompts until about ``budget_s`` of CPU work."""
-    import oracle
-    from oracle.prefill import default_threads
-    from workloads import to_f64
-
-    lens = np.array([s.n for s in call.segments])
-    wmean = float((lens ** 2).sum() / lens.sum())
-    order = np.argsort(np.abs(lens - wmean))
-    threads = default_threads()
-    done_tokens, spent, used = 0, 0.0, []
-    for i in order:
-        s = call.segments[int(i)]
-        a, b = int(call.cu_seqlens[i]), int(call.cu_seqlens[i + 1])
-        args = dict(segments=[(0, 0, s.n, True)], q=to_f64(call.q[a:b], "bf16"),
-                    k=to_f64(call.k[a:b], "bf16"), v=to_f64(call.v[a:b], "bf16"),
-                    positions=call.positions[a:b], cu_seqlens=[0, s.n], Hq=wl.Hq, Hkv=wl.Hkv,
-                    D=wl.D, theta=wl.theta, window=0, block_size=wl.block_size, p=wl.p,
-                    cache=oracle.KVCacheModel(),
-                    rows={"hidden": call.hidden[a:b], "positions": call.positions[a:b],
-                          "slot_mapping": call.slot_mapping[a:b]}, threads=threads)
-        t0 = time.perf_counter()
-        oracle.run_call(**args)
-        spent += time.perf_counter() - t0
-        done_tokens += s.n
-        used.append(s.n)
-        if spent >= budget_s:
-            break
-    return {"value": done_tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(used)} whole prompt(s) of the batch (lengths {used}, "
-                      f"{done_tokens} tokens) through rope, attention, scores, top-p and "
-                      f"compaction, float64 NumPy, {spent:.1f} s"}
 
 
 def run_propagation(args):
@@ -739,148 +848,128 @@ def main():
     if args.sweep:
         run_sweep(args)
         return
-    if args.workload != WORKLOAD:
-        run_other_workload(args)
+    if args.workload != "all":
+        run_one_workload(args)
         return
+    run_all(args)
 
+
+def _generate(names):
+    """Generate the workloads on background threads (numpy's bulk draws
+    release the interpreter lock), so the GPU measures one while the next is
+    drawn."""
+    from concurrent.futures import ThreadPoolExecutor
+    import workloads as W
+
+    ex = ThreadPoolExecutor(max_workers=3)
+    return ex, {n: ex.submit(W.make, n) for n in names}
+
+
+def run_one_workload(args):
+    """One workload (every call, timed as one step), with its oracle sample."""
+    import torch
+
+    import workloads as W
+    wl = W.make(args.workload)
+    if args.whole_prompt and args.workload != "chunked_128k":
+        raise SystemExit("--whole-prompt applies to chunked_128k (one prompt in chunks)")
+    st = Staged(torch, wl, whole=args.whole_prompt)
+    t = time_workload(torch, st, args.steps, args.warmup)
+    m = workload_metrics(st, t)
+    if args.whole_prompt:
+        pc = st.calls[-1][1]
+        nbp = int(pc.cu_blocks[-1].item())
+        keep = pc.keep[:nbp].cpu().numpy().astype(bool)
+        sc = pc.scores[:nbp].cpu().numpy()
+        hb = -(-wl.heavy_prefix // wl.block_size)  # blocks holding the heavy-hitter cluster
+        m["whole_prompt"] = {
+            "prompt_blocks": nbp, "kept_blocks": int(keep.sum()), "cluster_blocks": hb,
+            "cluster_blocks_kept": int(keep[:hb].sum()), "other_blocks_kept": int(keep[hb:].sum()),
+            "mean_score_cluster": float(sc[:hb].mean()), "mean_score_other": float(sc[hb:].mean()),
+            "kept_cached_tokens": int(pc.num_kept_slots.item()),
+            "kept_own_tokens": int(pc.num_kept.item())}
+    l2p = m["swa_layer"]["pairs"] if "swa_layer" in m else None
+    del st
+    torch.cuda.empty_cache()
+    res = {"metric": METRIC, "value": m["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic", "config": {"workload": f"{args.workload}: {DESCRIBE[args.workload]}"},
+           "roofline": dict(m["attention"], achieved=m["attention"]["TFLOP/s"],
+                            unit="TFLOP/s", traffic=None),
+           "detail": m}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = oracle_sample(wl, args.cpu_budget_s / 2, l2p)
+    print(json.dumps(res), flush=True)
+
+
+def run_all(args):
+    """The default run: the headline packed workload gives the bench line's
+    value, roofline and CPU baseline; every other workload is timed the same
+    way under ``configs``.  Inputs are generated on background threads while
+    the GPU measures; the oracle samples run afterwards on an idle host."""
+    import torch
     from block_sparse_token_amd import binding as B
 
-    wl, call, pc = headline_call(torch)
+    names = [n for n, *_ in CONFIGS]
+    ex, futs = _generate(names)
     stream = torch.cuda.current_stream()
-    K, Wm = args.steps, args.warmup
-
-    def ev():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)  # creates the underlying event
-        return e
-
-    for _ in range(Wm):
-        pc.launch()
-    torch.cuda.synchronize()
-    # per-step events: stage boundaries and the attention kernel itself
-    stage_ev = [[ev() for _ in range(5)] for _ in range(K)]
-    attn_ev = [(ev(), ev()) for _ in range(K)]
-    torch.cuda.synchronize()
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        e = stage_ev[i]
-        B.up_profile_attn_events(*attn_ev[i])
-        e[0].record(stream)
-        pc.attention()
-        e[1].record(stream)
-        pc.scores_stage()
-        e[2].record(stream)
-        pc.select_stage()
-        e[3].record(stream)
-        pc.compact_stage()
-        e[4].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    B.up_profile_attn_events()
-
-    ms_step = wall * 1e3 / K
-    T = call.T
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in attn_ev]))
-    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in stage_ev])
-    st_mean = st.mean(axis=0)
-    pairs = algorithmic_pairs(call)
-    flops = 4.0 * wl.D * wl.Hq * pairs
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    kept = int(pc.num_kept.item())
-    nb = call.num_blocks(wl.block_size)
-    W_bytes = wl.hidden_width * 2
-    compact_bytes = kept * (2 * W_bytes + 20) + nb
-    src_hash = kernel_code_hash(os.path.join(ROOT, "block_sparse_token_amd", "csrc", "attn_bf16.hip"))
-    res = {
-        "metric": "packed prefill tokens/s (attn+score+select+compact) + % MFMA/HBM roofline",
-        "value": T / (ms_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B-shaped packed prefill: 16 prompts U{512..8192} "
-                               f"(seed 2, {T} tokens), 32/8 heads x 128, bf16, rope 5e5, "
-                               "block 64, top-p 0.95, hidden 4096",
-                   "tokens": T, "segments": len(call.segments), "kept_tokens": kept},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic_from_profile(src_hash),
-                     "kernel": "attn_bf16_kernel", "avg_ms": attn_ms,
-                     "flops_per_launch": flops, "pairs": pairs},
-        "stages_ms": {"rope_kv+plan+attention": float(st_mean[0]), "scores": float(st_mean[1]),
-                      "select": float(st_mean[2]), "compact": float(st_mean[3])},
-        "compact_hbm": {"bytes": compact_bytes,
-                        "GB/s": compact_bytes / (st_mean[3] * 1e-3) / 1e9,
-                        "frac": compact_bytes / (st_mean[3] * 1e-3) / 1e9 / PEAK_HBM_GBS},
-    }
     att = attainable_peaks(torch, B, stream)
-    res["roofline"]["attainable"] = att["mfma_bf16_TFLOP/s"]
-    res["roofline"]["frac_of_attainable"] = achieved / att["mfma_bf16_TFLOP/s"]
-    res["attainable_peaks"] = att
-    res["compact_hbm"]["frac_of_attainable"] = res["compact_hbm"]["GB/s"] / att["hbm_copy_GB/s"]
-    # every pass against the HBM roofline, with its algorithmic bytes: the
-    # rotary/cache-write pass reads k, v and writes both to the cache (plus
-    # position and slot per token; the plan and block-mass kernels launched
-    # with it move a few MB); scores read the block mass and write one float
-    # per block; top-p reads the scores and writes a keep byte per block
-    # (plus per-segment counts); compaction as above
-    S = len(call.segments)
-    e_b = 2
-    pass_bytes = {
-        "rope_kv_plan_mass": (T * (4 * wl.Hkv * wl.D * e_b + 8), float(st_mean[0]) - attn_ms),
-        "scores": (4 * wl.Hq * nb + 4 * nb, float(st_mean[1])),
-        "select": (5 * nb + 4 * S, float(st_mean[2])),
-        "compact": (compact_bytes, float(st_mean[3])),
-    }
-    res["passes_hbm"] = {
-        k: {"us": ms * 1e3, "bytes": b, "GB/s": b / (ms * 1e-3) / 1e9,
-            "frac": b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "frac_of_attainable": b / (ms * 1e-3) / 1e9 / att["hbm_copy_GB/s"]}
-        for k, (b, ms) in pass_bytes.items()}
-    # the same passes with the 256 MB Infinity Cache flushed before every
-    # step (a 512 MiB buffer written in between, outside the timed stages),
-    # so no pass finds its inputs in that cache
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    fl_ev = []
-    for i in range(min(K, 10)):
-        flush.fill_(i & 255)
-        e = [ev() for _ in range(5)]
-        a_ev = (ev(), ev())
-        B.up_profile_attn_events(*a_ev)
-        e[0].record(stream)
-        pc.attention()
-        e[1].record(stream)
-        pc.scores_stage()
-        e[2].record(stream)
-        pc.select_stage()
-        e[3].record(stream)
-        pc.compact_stage()
-        e[4].record(stream)
-        fl_ev.append((e, a_ev))
-    torch.cuda.synchronize()
-    B.up_profile_attn_events()
-    del flush
-    st_fl = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e, _ in fl_ev]).mean(axis=0)
-    attn_fl = float(np.mean([a.elapsed_time(b) for _, (a, b) in fl_ev]))
-    fl_ms = {"rope_kv_plan_mass": float(st_fl[0]) - attn_fl, "scores": float(st_fl[1]),
-             "select": float(st_fl[2]), "compact": float(st_fl[3])}
-    for k, (b, _) in pass_bytes.items():
-        res["passes_hbm"][k].update({"us_cache_flushed": fl_ms[k] * 1e3,
-                                     "GB/s_cache_flushed": b / (fl_ms[k] * 1e-3) / 1e9,
-                                     "frac_cache_flushed": b / (fl_ms[k] * 1e-3) / 1e9 /
-                                     PEAK_HBM_GBS})
-    res["roofline"]["avg_ms_cache_flushed"] = attn_fl
-    res["library_attention"] = library_attention(torch, wl, call, pc, min(K, 5))
+    results, wls, l2pairs = {}, {}, {}
+    for name, label, cap_steps, cap_warm in CONFIGS:
+        wl = futs[name].result()
+        wls[name] = wl
+        K = args.steps if cap_steps is None else min(args.steps, cap_steps)
+        Wm = args.warmup if cap_warm is None else min(args.warmup, cap_warm)
+        print(f"measuring {label} {name} ({K} steps)", file=sys.stderr, flush=True)
+        st = Staged(torch, wl)
+        t = time_workload(torch, st, K, Wm)
+        m = workload_metrics(st, t)
+        m.update(label=label, workload=DESCRIBE[name], steps=K, warmup=Wm)
+        if name == WORKLOAD:
+            # the same passes with the Infinity Cache flushed before each step
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+            tf = time_workload(torch, st, min(K, 10), 0, flush=flush)
+            del flush
+            mf = workload_metrics(st, tf)
+            m["cache_flushed"] = {"attention_ms": tf["attn_ms"],
+                                  "passes": {k: v for k, v in mf["passes"].items()}}
+            if args.library:
+                call, pc = st.calls[0]
+                m["library_attention"] = library_attention(torch, wl, call, pc, min(K, 5))
+        l2pairs[name] = m["swa_layer"]["pairs"] if "swa_layer" in m else None
+        results[name] = m
+        del st
+        torch.cuda.empty_cache()
+    ex.shutdown(wait=True)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, call, args.cpu_budget_s)
+        for name, label, *_ in CONFIGS:
+            budget = args.cpu_budget_s if name == WORKLOAD else args.cpu_budget_s / 2
+            print(f"oracle sample {label}", file=sys.stderr, flush=True)
+            results[name]["cpu_baseline"] = oracle_sample(wls[name], budget, l2pairs[name])
+    h = results[WORKLOAD]
+    src_hash = kernel_code_hash(os.path.join(ROOT, "block_sparse_token_amd", "csrc",
+                                             "attn_bf16.hip"))
+    a = h["attention"]
+    res = {
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": h["steps"], "warmup": h["warmup"], "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: {DESCRIBE[WORKLOAD]} ({h['tokens']} tokens)",
+                   "tokens": h["tokens"], "kept_tokens": h["kept_tokens"]},
+        "roofline": {"bound": "mfma", "achieved": a["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": a["frac"],
+                     "traffic": traffic_from_profile(src_hash), "kernel": a["kernel"],
+                     "avg_ms": a["ms"], "flops_per_launch": a["flops"], "pairs": a["pairs"],
+                     "attainable": att["mfma_bf16_TFLOP/s"],
+                     "frac_of_attainable": a["TFLOP/s"] / att["mfma_bf16_TFLOP/s"]},
+        "passes_hbm": h["passes"],
+        "attainable_peaks": att,
+        "configs": {results[n]["label"]: results[n] for n in names},
+    }
+    if "cpu_baseline" in h:
+        res["cpu_baseline"] = h["cpu_baseline"]
     print(json.dumps(res), flush=True)
 
 

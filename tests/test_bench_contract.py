@@ -57,3 +57,33 @@ def test_kernel_hash_covers_the_files_compile_flags(tmp_path):
     copy = tmp_path / "same_source_no_flags.hip"
     copy.write_text(open(src).read())
     assert bench.kernel_code_hash(src) != bench.kernel_code_hash(str(copy))
+
+
+def test_oracle_sample_scales_by_visible_pairs():
+    """The CPU baseline's sample: the oracle on whole segments, its rate
+    scaled to the workload by visible (query, key) pairs; a workload that is
+    its own sample is not scaled."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    from oracle import driver
+
+    wl = W.make("small_chunked_fp32")
+    r = bench.oracle_sample(wl, 1.0)
+    assert r["kind"] == "oracle" and r["cores"] >= 1
+    assert abs(r["value"] - r["sample_tokens_per_s"]) <= 1e-9 * r["value"]
+    # several packed prompts: the sample runs some of them in one pass
+    wl = W.custom(lengths=[300, 120, 500, 64], Hq=4, Hkv=2, D=64, dtype="bf16", block_size=16,
+                  p=0.9, theta=500000.0, seed=2)
+    r = bench.oracle_sample(wl, 0.0)
+    n = int(r["sample"].split("lengths [")[1].split("]")[0])
+    pairs_all = sum(x * (x + 1) // 2 for x in [300, 120, 500, 64])
+    want = 984 / (r["sample_seconds"] * pairs_all / (n * (n + 1) // 2))
+    assert abs(r["value"] - want) <= 1e-9 * want
+    # the second layer's pairs are added to the workload's
+    wl = W.config_swa_after_selection(n_prompts=2, len_range=(150, 250))
+    res = driver.run_workload(wl, threads=2)[0]
+    cu2, pos2 = res["cu_seqlens_out"], res["rows_out"]["positions"]
+    p2 = bench.visible_pairs(cu2, np.zeros(len(cu2) - 1, np.int64), pos2, wl.layer2["window"])
+    r = bench.oracle_sample(wl, 0.0, p2)
+    assert r["value"] > 0 and "sliding-window" in r["sample"]

@@ -9,7 +9,9 @@ import workloads as W
 def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(0)
     x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10,
-                        np.array([1.0, -2.5, 3.0e-3, 65504.0, 1.00390625, 1.01171875], np.float32)])
+                        np.array([1.0, -2.5, 3.0e-3, 65504.0, 1.00390625, 1.01171875, 0.0, -0.0,
+                                  np.inf, -np.inf, 3.4028235e38, -3.4028235e38, 1e-45, -1e-45,
+                                  1.1754942e-38, -1.0039062], np.float32)])
     ours = W.f32_to_bf16_bits(x)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(ours, ref)

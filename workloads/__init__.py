@@ -33,11 +33,14 @@ GROUP = 16  # heavy-hitter group size in tokens
 # bf16 storage helpers (bit manipulation only)
 # ---------------------------------------------------------------------------
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits."""
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    The sum stays inside 32 bits for every finite value and for the
+    infinities (bit patterns below 0xFFFF8000); the generators draw no NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    lsb = (b >> np.uint64(16)) & np.uint64(1)
-    r = (b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    b = x.view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    r = (b + (np.uint32(0x7FFF) + lsb)) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
