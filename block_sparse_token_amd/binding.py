@@ -64,6 +64,9 @@ def lib():
             "up_prefill_attn": (c_i32, [bp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_f32, c_i32, c_f32, c_vp, c_i32, c_i32, c_vp, c_vp,
                                         c_vp, c_vp, c_vp, c_size, c_vp]),
+            "up_prefill_attn_noalloc": (c_i32, [bp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                                                c_vp, c_vp, c_f32, c_i32, c_f32, c_vp, c_i32,
+                                                c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "up_block_scores": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
             "up_topp_select": (c_i32, [bp, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp, c_vp]),
             "up_score_select": (c_i32, [bp, c_i32, c_i32, c_vp, c_vp, c_f64, c_vp, c_vp, c_vp,
@@ -100,7 +103,8 @@ EXPORTED = ["up_last_error", "up_version", "up_block_offsets", "up_attn_workspac
             "up_compact", "up_profile_attn_events", "up_check_batch", "up_peak_mfma_bf16",
             "up_peak_copy", "up_linear_bf16", "up_linear_attn_bf16", "up_kept_cache_slots",
             "up_linear_attn_workspace_bytes", "up_linear_attn_bf16_parts", "up_score_select",
-            "up_profile_rope_events"]
+            "up_profile_rope_events", "up_prefill_attn_noalloc"]
+UP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def _check(st: int, what: str):
@@ -184,6 +188,24 @@ def up_prefill_attn(batch: Batch, q, k, v, k_cache, v_cache, out, workspace, *, 
                                  _p(block_mass), _p(out), _p(lse), _p(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "up_prefill_attn")
+
+
+def up_prefill_attn_noalloc(batch: Batch, q, k, v, k_cache, v_cache, out, *, rope_theta=0.0,
+                            window=0, sm_scale=0.0, score_flags=None, block_size=0,
+                            score_scope=UP_SCOPE_SEGMENT, cu_blocks=None, block_mass=None,
+                            lse=None, stream=None):
+    """up_prefill_attn without a workspace: the library's per-GPU scratch
+    array serves instead (calls that overlap on one GPU race)."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if q.dtype not in _DT or any(t.dtype != q.dtype for t in (k, v, k_cache, v_cache, out)):
+        raise UniprefillError("q, k, v, caches and out must share one dtype (float32 or bfloat16)")
+    _check(lib().up_prefill_attn_noalloc(batch.ref, _DT[q.dtype], Hq, Hkv, D, _p(q), _p(k),
+                                         _p(v), _p(k_cache), _p(v_cache), float(rope_theta),
+                                         int(window), float(sm_scale), _p(score_flags),
+                                         int(block_size), int(score_scope), _p(cu_blocks),
+                                         _p(block_mass), _p(out), _p(lse), _stream(stream)),
+           "up_prefill_attn_noalloc")
 
 
 def up_block_scores(batch: Batch, Hq, block_size, cu_blocks, score_flags, block_mass, scores,

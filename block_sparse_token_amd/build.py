@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "plan.hip", "rope_kv.hip", "attn_bf16.hip", "attn_f32.hip", "select.hip",
            "compact.hip", "peaks.hip", "mass.hip", "linear.hip",
-           "linear_attn.hip"]
+           "linear_attn.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -9,6 +9,9 @@
 #include "../../include/uniprefill.h"
 #include "common.h"
 
+static_assert(UP_NOALLOC_SCRATCH_BYTES == up::kNoAllocScratchBytes,
+              "the header states the no-allocation scratch size");
+
 namespace {
 
 thread_local std::string g_err;
@@ -304,12 +307,16 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
   return bytes;
 }
 
-up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
-                          int32_t D, const void* q, const void* k, const void* v, void* k_cache,
-                          void* v_cache, float rope_theta, int32_t window, float sm_scale,
-                          const uint8_t* score_flags, int32_t block_size, int32_t score_scope,
-                          const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// The attention call with its scratch in `workspace`: a caller's buffer, or
+// (noalloc) the library's per-device scratch array.
+up_status prefill_attn_impl(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                            int32_t D, const void* q, const void* k, const void* v,
+                            void* k_cache, void* v_cache, float rope_theta, int32_t window,
+                            float sm_scale, const uint8_t* score_flags, int32_t block_size,
+                            int32_t score_scope, const int32_t* cu_blocks, float* block_mass,
+                            void* out, float* lse, void* workspace, size_t workspace_bytes,
+                            void* stream, bool noalloc) {
   up_status st = check_batch(batch, true);
   if (st) return st;
   st = check_scope(batch, score_scope);
@@ -331,8 +338,11 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
        ((uintptr_t)v_cache) | ((uintptr_t)out)) & 15)
     return fail(UP_ERR_INVALID, "q, k, v, k_cache, v_cache and out must be 16-byte aligned");
   if (((uintptr_t)lse) & 3) return fail(UP_ERR_INVALID, "lse must be 4-byte aligned");
-  if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
-  if (((uintptr_t)workspace) & 15) return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (!noalloc) {
+    if (!workspace) return fail(UP_ERR_INVALID, "workspace is NULL");
+    if (((uintptr_t)workspace) & 15)
+      return fail(UP_ERR_INVALID, "workspace must be 16-byte aligned");
+  }
   if (!(rope_theta == rope_theta) || !(sm_scale == sm_scale))
     return fail(UP_ERR_INVALID, "rope_theta and sm_scale must not be NaN");
   if (score_flags) {
@@ -349,6 +359,18 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
                 batch->num_seqs);
   const size_t need =
       up_attn_workspace_bytes(batch, dtype, Hq, Hkv, D, score_flags ? block_size : 0, score_scope);
+  if (noalloc) {
+    if (need > up::kNoAllocScratchBytes)
+      return fail(UP_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                  "(fewer tokens, segments or cached pages per call, or up_prefill_attn with a "
+                  "workspace)",
+                  need, up::kNoAllocScratchBytes);
+    // the GPU's scratch array, after every argument check
+    const hipError_t e = up::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return device_status(e, "no-allocation scratch lookup");
+    workspace_bytes = up::kNoAllocScratchBytes;
+  }
   if (workspace_bytes < need)
     return fail(UP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
 
@@ -450,6 +472,30 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
     if (e != hipSuccess) return device_status(e, "block mass launch");
   }
   return UP_OK;
+}
+
+}  // namespace
+
+up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                          int32_t D, const void* q, const void* k, const void* v, void* k_cache,
+                          void* v_cache, float rope_theta, int32_t window, float sm_scale,
+                          const uint8_t* score_flags, int32_t block_size, int32_t score_scope,
+                          const int32_t* cu_blocks, float* block_mass, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_attn_impl(batch, dtype, Hq, Hkv, D, q, k, v, k_cache, v_cache, rope_theta,
+                           window, sm_scale, score_flags, block_size, score_scope, cu_blocks,
+                           block_mass, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+up_status up_prefill_attn_noalloc(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                                  int32_t D, const void* q, const void* k, const void* v,
+                                  void* k_cache, void* v_cache, float rope_theta, int32_t window,
+                                  float sm_scale, const uint8_t* score_flags, int32_t block_size,
+                                  int32_t score_scope, const int32_t* cu_blocks,
+                                  float* block_mass, void* out, float* lse, void* stream) {
+  return prefill_attn_impl(batch, dtype, Hq, Hkv, D, q, k, v, k_cache, v_cache, rope_theta,
+                           window, sm_scale, score_flags, block_size, score_scope, cu_blocks,
+                           block_mass, out, lse, nullptr, 0, stream, true);
 }
 
 up_status up_block_scores(const up_batch* batch, int32_t Hq, int32_t block_size,

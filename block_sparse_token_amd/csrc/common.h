@@ -13,6 +13,8 @@ constexpr int kPageSize = 16;
 constexpr int kMaxSeqsPlan = 4096;  // segments per call the work planner handles
 constexpr int kMaxRopePairs = 64;   // D / 2 for D = 128
 constexpr int kMaxBlockSize = 256;  // block sizes: multiples of 16 in [16, 256]
+// scratch of the no-allocation attention entry point, per GPU
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 
 // The bf16 attention sweep records the log2-sum-exp of every run of this
 // many consecutive scored keys (a run never straddles a 64-key tile, and a
@@ -107,6 +109,9 @@ hipError_t launch_check_batch(const int32_t* cu_seqlens, const int32_t* ctx_lens
                               int T, int max_pages, int num_pages, int grid, int32_t* err,
                               hipStream_t st);
 // blocks_cap: at least cu_blocks[S] (workgroups past it exit at once)
+// Device address of this GPU's no-allocation scratch (kNoAllocScratchBytes,
+// 256-byte aligned); looked up once per device, with that device current.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_block_mass(const AttnArgs& a, int S, int blocks_cap, hipStream_t st);
 hipError_t launch_peak_mfma(int workgroups, int iters, float* sink, hipStream_t st);
 hipError_t launch_peak_copy(const void* src, void* dst, size_t bytes, hipStream_t st);

@@ -198,6 +198,29 @@ up_status up_prefill_attn(const up_batch* batch, up_dtype dtype, int32_t Hq, int
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same attention call for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results as up_prefill_attn, without
+ * the workspace.  Its scratch (work list, queue counters, per-run score
+ * sums) is a device array of UP_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing and frees nothing.  A call that needs more scratch than that
+ * (up_attn_workspace_bytes for the same arguments) returns
+ * UP_ERR_WORKSPACE and launches nothing.  Every call on one GPU uses the
+ * same array, so calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race and give wrong results;
+ * calls ordered on one stream are safe.  Nothing in the scratch has to start
+ * at zero.
+ */
+#define UP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+up_status up_prefill_attn_noalloc(const up_batch* batch, up_dtype dtype, int32_t Hq, int32_t Hkv,
+                                  int32_t D, const void* q, const void* k, const void* v,
+                                  void* k_cache, void* v_cache, float rope_theta, int32_t window,
+                                  float sm_scale, const uint8_t* score_flags, int32_t block_size,
+                                  int32_t score_scope, const int32_t* cu_blocks,
+                                  float* block_mass, void* out, float* lse, void* stream);
+
+/*
  * Block scores (UniPrefill review, "Method & Key Results": an importance per
  * token block, estimated at a full-attention layer; "Key Terms &
  * Definitions", Top-p Token Selection: importances normalised so that

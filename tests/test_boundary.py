@@ -17,7 +17,7 @@ from block_sparse_token_amd import binding as Bd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "uniprefill.h")
 
-UP_OK, UP_ERR_INVALID, UP_ERR_UNSUPPORTED, UP_ERR_WORKSPACE = 0, -1, -2, -3
+UP_OK, UP_ERR_INVALID, UP_ERR_UNSUPPORTED, UP_ERR_WORKSPACE, UP_ERR_DEVICE = 0, -1, -2, -3, -4
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
@@ -102,6 +102,28 @@ def test_attention_argument_validation(L):
     nb = _batch(with_ptrs=False)
     assert _attn(L, nb) == UP_ERR_INVALID
     assert b"NULL" in L.up_last_error()
+
+
+def test_noalloc_entry_refuses_before_any_device_call(L):
+    """The no-allocation attention entry validates like up_prefill_attn and
+    refuses a call needing more than its scratch array, all on the host
+    (this container has no GPU: a device call would report UP_ERR_DEVICE)."""
+    def na(b, **k):
+        return L.up_prefill_attn_noalloc(ctypes.byref(b), 1, 32, 8, 128, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, 1e4, 0, 0.0, k.get("flags", FAKE), 64, 0, FAKE,
+                                         FAKE, FAKE, None, None)
+    b = _batch(S=2, T=600000)
+    assert L.up_attn_workspace_bytes(ctypes.byref(b), 1, 32, 8, 128, 64, 0) > Bd.UP_NOALLOC_SCRATCH_BYTES
+    assert na(b) == UP_ERR_WORKSPACE
+    msg = L.up_last_error().decode()
+    assert "bytes of scratch" in msg and str(Bd.UP_NOALLOC_SCRATCH_BYTES) in msg
+    assert na(_batch(S=0)) == UP_ERR_INVALID
+    bad = _batch(S=2, T=100)
+    assert L.up_prefill_attn_noalloc(ctypes.byref(bad), 1, 6, 4, 128, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     1e4, 0, 0.0, None, 0, 0, None, None, FAKE, None,
+                                     None) == UP_ERR_INVALID
+    # a call that fits gets past validation and only then needs the device
+    assert na(_batch(S=2, T=100)) == UP_ERR_DEVICE
 
 
 def test_workspace_size_arithmetic(L):
