@@ -14,7 +14,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libuniprefill.so")
+# UNIPREFILL_LIB selects another build of the library (the tests load the
+# host-sanitized one this way); by default the in-tree build.
+LIB_PATH = os.environ.get("UNIPREFILL_LIB") or os.path.join(HERE, "libuniprefill.so")
 
 UP_F32, UP_BF16 = 0, 1
 UP_SCOPE_SEGMENT, UP_SCOPE_PROMPT = 0, 1

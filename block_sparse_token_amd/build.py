@@ -40,11 +40,22 @@ FILE_FLAGS = {
 }
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizer build (tests only): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code of every source (argument
+# validation, workspace carving, launch set-up); device code is compiled as
+# usual.  Each sanitizer flag applies to the host pass only.
+SAN_DIR = os.path.join(ROOT, "_build_san")
+SAN_LIB = os.path.join(SAN_DIR, "libuniprefill_san.so")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src: str, out_dir: str = None, extra=()) -> str:
+    obj = os.path.join(out_dir or BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o",
+           obj]
     if src.endswith(".cpp"):
-        cmd = [HIPCC, "-O2", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+        cmd = [HIPCC, "-O2", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-c",
                os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -67,6 +78,33 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build the host-sanitized library at SAN_LIB (load it with the clang
+    AddressSanitizer runtime preloaded)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda f: _compile(f, SAN_DIR, ["-g", *SAN_HOST]), SOURCES))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SAN_LIB, *objs, *SAN_HOST,
+           "-Xarch_host", "-shared-libsan", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized library links against."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -64,7 +64,12 @@ typedef int up_status;
 #define UP_ERR_WORKSPACE (-3)   /* workspace smaller than the size query says    */
 #define UP_ERR_DEVICE (-4)      /* a HIP launch failed; text has hipGetErrorString */
 
-typedef enum { UP_F32 = 0, UP_BF16 = 1 } up_dtype;
+/* Element type of q, k, v, the caches and out.  A plain integer rather than
+ * an enum, so that any value a caller passes is well defined and can be
+ * refused (UP_ERR_UNSUPPORTED). */
+typedef int32_t up_dtype;
+#define UP_F32 0
+#define UP_BF16 1
 
 /* Text describing the last non-OK status returned on this thread. */
 const char* up_last_error(void);
