@@ -2,12 +2,13 @@
 (up_linear_attn_bf16) with the float64 oracle (oracle.linear_attention, the
 recurrent form).
 
-Tolerance: the bf16 output bound, |gpu - oracle| <= 2e-2 per element.  The
-GPU takes phi(q), phi(k) and the chunk's weights in bf16 (relative error
-2^-9 each) and the running state as a bf16 pair (about 2^-17); with v ~
-N(0, 1) the outputs are weighted means of values, so these relative
-errors of the weights move an output by a small fraction of the values'
-spread.
+Tolerance: the bf16 output bounds of the attention tests (``parity_checks``):
+|gpu - oracle| <= 2e-2 per element, and <= 2^-6 of the row's largest
+|oracle| (a row: one token and head) plus 1e-6.  The outputs are weighted
+means of values, so along a long segment they shrink like 1/sqrt(rows) and
+the absolute bound alone loses its power; the GPU's own error is relative
+to them: phi(q), phi(k) and the chunk's weights in bf16 (2^-9 each), the
+running state as a bf16 pair (about 2^-17).
 """
 import numpy as np
 import pytest
@@ -18,11 +19,10 @@ import workloads as W
 from block_sparse_token_amd import binding as Bd
 from block_sparse_token_amd import step as ST
 
-from gpu_harness import log
+from gpu_harness import check_bf16_values, log
 
 pytestmark = pytest.mark.gpu
 
-ABS = 2e-2
 SENTINEL = -12288.0
 
 
@@ -59,9 +59,9 @@ def _run(lengths, Hq, Hkv, seed, lead=0, tail=0, strided=False, parts=False):
     ref = oracle.linear_attention(W.to_f64(qb[a:b], "bf16"), W.to_f64(kb[a:b], "bf16"),
                                   W.to_f64(vb[a:b], "bf16"), cu - a)
     err = np.abs(got[a:b] - ref)
-    log(f"  max abs err {err.max():.3e}, rms out {np.sqrt(np.mean(ref ** 2)):.3e}")
-    assert np.all(np.isfinite(got[a:b]))
-    assert err.max() <= ABS
+    ratio = check_bf16_values(got[a:b], ref, "linear attention")
+    log(f"  max abs err {err.max():.3e}, rms out {np.sqrt(np.mean(ref ** 2)):.3e}, "
+        f"worst / row-relative bound {ratio:.3f}")
     assert np.all(got[:a] == SENTINEL) and np.all(got[b:] == SENTINEL)
 
 
@@ -119,9 +119,11 @@ def test_gpu_linear_attention_headline_batch_sampled_segments(parts):
     for s in sorted({0, longest, len(lengths) - 1}):
         a, b = int(cu[s]), int(cu[s + 1])
         ref = oracle.linear_attention(_f64(q[a:b]), _f64(k[a:b]), _f64(v[a:b]), [0, b - a])
-        err = float(np.abs(_f64(out[a:b]) - ref).max())
-        log(f"  segment {s} ({b - a} tokens): max abs err {err:.3e}")
-        assert err <= ABS
+        got = _f64(out[a:b])
+        err = float(np.abs(got - ref).max())
+        ratio = check_bf16_values(got, ref, f"segment {s}")
+        log(f"  segment {s} ({b - a} tokens): max abs err {err:.3e}, worst / row-relative "
+            f"bound {ratio:.3f}")
     assert not bool((out == SENTINEL).any()), "a row inside the segments was not written"
 
 
@@ -144,7 +146,9 @@ def test_gpu_linear_attention_parts_one_long_segment():
     Bd.up_linear_attn_bf16(cu, q, k, v, out, workspace=_workspace(rows, 1, Hq))
     torch.cuda.synchronize()
     ref = oracle.linear_attention(_f64(q[:, :1]), _f64(k[:, :1]), _f64(v[:, :1]), [0, rows])
-    err = np.abs(_f64(out[:, :1]) - ref)
-    log(f"  head 0: max abs err {err.max():.3e} (worst row {int(err.max(axis=(1, 2)).argmax())})")
-    assert err.max() <= ABS
+    got = _f64(out[:, :1])
+    err = np.abs(got - ref)
+    ratio = check_bf16_values(got, ref, "head 0")
+    log(f"  head 0: max abs err {err.max():.3e} (worst row {int(err.max(axis=(1, 2)).argmax())}), "
+        f"worst / row-relative bound {ratio:.3f}")
     assert not bool((out == SENTINEL).any()), "a row was not written"
