@@ -286,8 +286,12 @@ __device__ inline void load_q(const AttnArgs& a, long qrow_elem, bool valid, int
     for (int kc = 0; kc < C::KC / 2; ++kc) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = kc * 16 + h * 8 + e;
-        double t = (double)pos * a.rope_rev[j];
+        // the frequency of pair j = kc*16 + h*8 + e, read at indices that
+        // are the same in every lane (scalar loads of the argument) and
+        // selected by h; an index that depends on the lane would make every
+        // lane load its frequencies from memory after its q loads
+        const double rev0 = a.rope_rev[kc * 16 + e], rev1 = a.rope_rev[kc * 16 + 8 + e];
+        double t = (double)pos * (h ? rev1 : rev0);
         t -= rint(t);
         const float s = __builtin_amdgcn_sinf((float)t);
         const float c = __builtin_amdgcn_cosf((float)t);
