@@ -19,7 +19,10 @@ flops 4 * D * Hq * (visible query/key pairs) per launch over its average
 duration, timed with HIP events the library records around that kernel on
 its stream; ``attainable`` beside the published ``peak`` is what a plain
 bf16 matrix-core loop sustains on the same GPU in the same run.  Every other
-pass is set against HBM with the bytes it must move (``passes``).
+pass is set against HBM with the bytes it must move (``passes``), and the
+rotary/cache-write and compaction passes also against a plain streaming copy
+of the same bytes per call (``copy_us_same_bytes``, ``frac_of_copy``): at a
+few tens of MB a copy's own launch and ramp keep it well below the HBM peak.
 ``cpu_baseline`` is the float64 NumPy oracle timed on this host on a bounded
 sample of the same workload, scaled to the whole workload by visible pairs.
 """
@@ -472,6 +475,46 @@ def attainable_peaks(torch, B, stream):
                       "up_peak_copy (1 GiB read + 1 GiB written), medians of event-timed launches"}
 
 
+def copy_us_same_bytes(torch, B, stream, nbytes, cache):
+    """Median event-timed duration (us) of the library's streaming copy
+    (``up_peak_copy``) moving ``nbytes`` in all, half read and half written:
+    what a plain copy of a pass's size sustains, launch and ramp included."""
+    half = max(4096, (int(nbytes) // 2) // 4096 * 4096)
+    if half not in cache:
+        src = torch.ones(half // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        B.up_peak_copy(src, dst)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(10):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            B.up_peak_copy(src, dst)
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        if not torch.equal(dst[:: 1 << 16], src[:: 1 << 16]):
+            raise RuntimeError("peak copy produced wrong data")
+        del src, dst
+        cache[half] = float(np.median(ms)) * 1e3
+    return cache[half]
+
+
+def add_copy_comparison(torch, B, stream, m, cache):
+    """For each HBM pass of a workload: the time a plain copy of the same
+    bytes per call takes (times the number of calls) and the pass's rate as
+    a fraction of that copy's."""
+    calls = m["calls"]
+    for name in ("rope_kv_write", "compact"):
+        p = m["passes"][name]
+        if not p["bytes"] or not p["us"]:
+            continue
+        c_us = calls * copy_us_same_bytes(torch, B, stream, p["bytes"] / calls, cache)
+        p["copy_us_same_bytes"] = c_us
+        p["frac_of_copy"] = c_us / p["us"]
+
+
 def headline_call(torch, p=None):
     """The headline workload's one call, staged on the GPU: inputs, caches,
     batch metadata, and the hidden states, positions and KV slots to compact
@@ -915,7 +958,7 @@ def run_all(args):
     ex, futs = _generate(names)
     stream = torch.cuda.current_stream()
     att = attainable_peaks(torch, B, stream)
-    results, wls, l2pairs = {}, {}, {}
+    results, wls, l2pairs, copy_cache = {}, {}, {}, {}
     for name, label, cap_steps, cap_warm in CONFIGS:
         wl = futs[name].result()
         wls[name] = wl
@@ -941,6 +984,7 @@ def run_all(args):
         results[name] = m
         del st
         torch.cuda.empty_cache()
+        add_copy_comparison(torch, B, stream, m, copy_cache)
     ex.shutdown(wait=True)
     if not args.no_cpu_baseline:
         for name, label, *_ in CONFIGS:

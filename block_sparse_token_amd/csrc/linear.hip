@@ -219,8 +219,11 @@ hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int rows_ca
   a.act = act;
   a.tiles_m = (rows_cap + kBM - 1) / kBM;
   a.tiles_n = N / kBN;
+  // chunk shape CM x CN = 32 tiles: an XCD's L2 fetches CM + CN panels per
+  // chunk, fewest for the squarest shape (4 x 8 = 12 panels, against 18 for
+  // 2 x 16), so CN is the first of 8, 4, 16, 2 that divides the feature tiles
   a.cn = 1;
-  for (int c = 16; c > 1; c /= 2)
+  for (int c : {8, 4, 16, 2})
     if (a.tiles_n % c == 0) {
       a.cn = c;
       break;
