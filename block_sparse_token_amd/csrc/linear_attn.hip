@@ -17,16 +17,23 @@
 //   A   = mask(phi(Q_c) phi(K_c)^T)           (64 x 64, key <= query)
 //   o_c = (A V_c + phi(Q_c) S) / (A 1 + phi(Q_c) z)
 //   S  += phi(K_c)^T V_c,   z += phi(K_c)^T 1
-// All four products run on v_mfma_f32_32x32x16_bf16.  S stays in float32
+// All products run on v_mfma_f32_32x32x16_bf16, the row sums A 1 and the
+// key sums phi(K_c)^T 1 too (against a ones operand).  S stays in float32
 // registers (wave w owns output columns 32w..32w+31, which are the columns
 // of the outputs it computes); the product phi(Q_c) S takes it from there
 // as the bf16 pair hi + lo (hi the rounding of S, lo that of the
 // remainder), so S enters with about 16 significant bits.  With no copy of
-// S in LDS, two workgroups share a compute unit.  The denominators use the same bf16 A and phi(K) as the
-// numerators.  LDS tiles are row-major with 16-byte chunks XOR-swizzled per
-// row, so fragment reads of 16 rows fall on distinct banks; phi(K) and V
-// are also stored transposed (key-minor), which is the layout the products
-// over keys read.
+// S in LDS, two workgroups share a compute unit.  The denominators use the
+// same bf16 A and phi(K) as the numerators.
+//
+// LDS: phi(Q), phi(K) and V are stored token-major as loaded (16-byte
+// stores), A as A^T (key-major, 8-byte stores from the product's
+// accumulator).  Products that contract over tokens or keys take their
+// operands with ds_read_b64_tr_b16 transpose reads: two reads give a lane
+// the 8 keys {4h..4h+3, 8+4h..8+4h+3} of a 16-key step (h = lane / 32),
+// the same permutation on both operands.  The 16-byte chunks of a row are
+// XOR-swizzled so that both the row reads (16 rows of one chunk) and the
+// transpose reads (4 rows of a 64-byte chunk group) fall on distinct banks.
 #include "common.h"
 #include "lds_copy.h"
 
@@ -38,6 +45,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const bf16x8 lbf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lbf16x4;
 
 constexpr int kC = 64;   // tokens per chunk
 constexpr int kD = 128;  // head dimension
@@ -45,18 +53,39 @@ constexpr int kThreads = 256;
 // LDS layout (bytes)
 constexpr int QF = 0;                  // phi(Q) [64][128]   rows of 256 B
 constexpr int KF = QF + kC * kD * 2;   // phi(K) [64][128]
-constexpr int KT = KF + kC * kD * 2;   // phi(K)^T [128][64] rows of 128 B
-constexpr int VT = KT + kD * kC * 2;   // V^T [128][64]
-constexpr int AB = VT + kD * kC * 2;   // A [64][64]         rows of 128 B
-constexpr int ZF = AB + kC * kC * 2;   // z [128] f32
-constexpr int DN = ZF + kD * 4;        // denominators [64] f32
+constexpr int VF = KF + kC * kD * 2;   // V [64][128]
+constexpr int AT = VF + kC * kD * 2;   // A^T [64 keys][64 queries], rows of 128 B
+constexpr int ZF = AT + kC * kC * 2;   // z [128] f32
+constexpr int DN = ZF + kD * 4;        // phi(Q) . z per row [64] f32
 constexpr int kLdsBytes = DN + kC * 4;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per compute unit");
 
+// chunk swizzles: 256-byte rows (16 chunks): (r & 3) picks the 64-byte
+// chunk group and (r >> 2) & 3 the chunk in it, a bijection over any 16
+// consecutive rows that sends 4 consecutive rows to 4 different groups;
+// 128-byte rows (8 chunks): rows r and r + 2 in different 64-byte groups,
+// (r >> 2) & 3 inside the group
+__device__ inline int sw256(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ inline int sw128(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 // byte offset of element (r, e) in a row-major bf16 tile with 256-byte rows
-__device__ inline int off256(int r, int e) { return r * 256 + ((((e >> 3) ^ (r & 15))) << 4) + (e & 7) * 2; }
+__device__ inline int off256(int r, int e) { return r * 256 + (((e >> 3) ^ sw256(r)) << 4) + (e & 7) * 2; }
 // ... with 128-byte rows
-__device__ inline int off128(int r, int e) { return r * 128 + ((((e >> 3) ^ ((r >> 1) & 7))) << 4) + (e & 7) * 2; }
+__device__ inline int off128(int r, int e) { return r * 128 + (((e >> 3) ^ sw128(r)) << 4) + (e & 7) * 2; }
+
+// The 8 keys (tokens) {k0 + 4h + 0..3, k0 + 8 + 4h + 0..3} of column
+// c0 + lane % 32 of a token-major tile (element offsets from `off`), by two
+// transpose reads: in each 16-lane group, lane 4a + b points at row
+// k0 + 4h + a (then + 8), columns c0 + 16 ((lane >> 4) & 1) + 4b.. + 3, and
+// receives column c0 + lane % 32 of those four rows.
+template <int (*OFF)(int, int)>
+__device__ inline bf16x8 tr_frag(uint32_t base, int k0, int c0) {
+  const int l = threadIdx.x & 63, h = l >> 5;
+  const int r = k0 + 4 * h + ((l & 15) >> 2);
+  const int c = c0 + (l & 16) + 4 * (l & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4*)(uintptr_t)(base + OFF(r, c)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lbf16x4*)(uintptr_t)(base + OFF(r + 8, c)));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 
 __device__ inline float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
@@ -141,27 +170,41 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
   __syncthreads();
 
   // the chunk's raw q, k, v rows: thread tid handles (row p / 16, 16-byte
-  // column chunk p % 16) for p = tid + 256 i
+  // column chunk p % 16) for p = tid + 256 i (q only where outputs are made)
   u32x4 rq[4], rk[4], rv[4];
-  auto load_chunk = [&](int t0) {
+  auto load_q = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + kThreads * i, r = p >> 4, c = p & 15;
-      rq[i] = rk[i] = rv[i] = u32x4{0u, 0u, 0u, 0u};
+      rq[i] = u32x4{0u, 0u, 0u, 0u};
+      if (MODE != 1 && t0 + r < t_end)
+        rq[i] = *(const u32x4*)(a.q + (long)(t0 + r) * a.q_stride + (long)h * kD + c * 8);
+    }
+  };
+  auto load_kv = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + kThreads * i, r = p >> 4, c = p & 15;
+      rk[i] = rv[i] = u32x4{0u, 0u, 0u, 0u};
       if (t0 + r < t_end) {
         const long t = t0 + r;
-        if (MODE != 1) rq[i] = *(const u32x4*)(a.q + t * a.q_stride + (long)h * kD + c * 8);
         rk[i] = *(const u32x4*)(a.k + t * a.k_stride + (long)g * kD + c * 8);
         rv[i] = *(const u32x4*)(a.v + t * a.v_stride + (long)g * kD + c * 8);
       }
     }
   };
+  const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                       (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
+  if (MODE == 1) load_kv(t_begin);
   for (int t0 = t_begin; t0 < t_end; t0 += kC) {
     const int nrows = min(kC, t_end - t0);
-    load_chunk(t0);
-    // (a) the chunk's phi(q), phi(k), v into LDS; rows past the segment are
-    // zero (not phi(0)), so they add nothing to A, S or z
+    if (MODE != 1) {
+      load_q(t0);
+      load_kv(t0);
+    }
+    // (a) the chunk's phi(q), phi(k), v into LDS, token-major; rows past
+    // the segment are zero (not phi(0)), so they add nothing to A, S or z
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + kThreads * i, r = p >> 4, c = p & 15;
@@ -169,27 +212,24 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
       bf16x8 fq, fk;
       const uint16_t* q16 = (const uint16_t*)&rq[i];
       const uint16_t* k16 = (const uint16_t*)&rk[i];
-      const uint16_t* v16 = (const uint16_t*)&rv[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         fq[e] = ok ? (__bf16)phi(bf2f(q16[e])) : (__bf16)0.f;
         fk[e] = ok ? (__bf16)phi(bf2f(k16[e])) : (__bf16)0.f;
       }
-      if (MODE != 1) {
-        *(bf16x8*)(lds + QF + off256(r, c * 8)) = fq;
-        *(bf16x8*)(lds + KF + off256(r, c * 8)) = fk;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *(__bf16*)(lds + KT + off128(c * 8 + e, r)) = fk[e];
-        *(uint16_t*)(lds + VT + off128(c * 8 + e, r)) = v16[e];
-      }
+      if (MODE != 1) *(bf16x8*)(lds + QF + off256(r, c * 8)) = fq;
+      *(bf16x8*)(lds + KF + off256(r, c * 8)) = fk;
+      *(u32x4*)(lds + VF + off256(r, c * 8)) = rv[i];
     }
+    // part sums: the next chunk's rows are loaded while this one is
+    // computed (the outputs' registers leave no room for that elsewhere)
+    if (MODE == 1 && t0 + kC < t_end) load_kv(t0 + kC);
     __syncthreads();
 
     if (MODE != 1) {
-    // (b) wave w: A block (rows 32 (w >> 1).., keys 32 (w & 1)..), masked,
-    // to LDS in bf16
+    // (b) wave w: block of A (query rows 32 (w >> 1).., keys 32 (w & 1)..),
+    // masked, to LDS as A^T in bf16 (a lane holds 4 consecutive queries of
+    // one key: 8-byte stores)
     {
       const int mr = w >> 1, nc = w & 1;
       f32x16 acc2[2];
@@ -204,26 +244,21 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
       const f32x16 acc = acc2[0] + acc2[1];
       const int key = nc * 32 + l32;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 v4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int row = mr * 32 + jj * 8 + hl * 4 + e;
-          *(__bf16*)(lds + AB + off128(row, key)) = (__bf16)(key <= row ? acc[jj * 4 + e] : 0.f);
+          v4[e] = (__bf16)(key <= row ? acc[jj * 4 + e] : 0.f);
         }
+        *(bf16x4*)(lds + AT + off128(key, mr * 32 + jj * 8 + hl * 4)) = v4;
+      }
     }
-    __syncthreads();
-
-    // (c) denominators: row r = tid / 4, quarter x = tid % 4 sums A[r][16x..]
-    // and phi(Q)[r][32x..] . z (z of the chunks before this one)
+    // (c) phi(Q) . z per row (z of the chunks before this one): row
+    // r = tid / 4, quarter x = tid % 4 of the head dimension
     {
       const int r = tid >> 2, x = tid & 3;
       float d = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 av = *(const bf16x8*)(lds + AB + off128(r, x * 16 + j * 8));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += (float)av[e];
-      }
       const float* z = (const float*)(lds + ZF) + x * 32;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -238,25 +273,30 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
     }
     __syncthreads();
 
-    // (d) wave w: outputs of columns 32w.. for both 32-row blocks:
-    // A V + phi(Q) S, divided by the row's denominator.  S comes from this
-    // wave's own registers: for the 16 rows of step ks, lane (c, half 0)
-    // holds rows 8jj + 0..3 of column c and lane (c, half 1) rows 8jj +
-    // 4..7; one v_permlane32_swap per register pair gives each lane the 8
-    // consecutive rows the product reads, split into bf16 hi + lo.
+    // (d) wave w: the transposed outputs O^T = V^T A^T + S^T phi(Q)^T of
+    // head dimensions 32w.. for both 32-query blocks, over A 1 + phi(Q) z.
+    // A lane then holds 16 dimensions of one query (4 consecutive per
+    // register group: 8-byte stores) and needs one denominator per block.
+    // V^T and A^T come by transpose reads (keys permuted alike); A 1 from
+    // the same A fragments against ones.  S^T comes from this wave's own
+    // registers: for the 16 rows of step ks of S, the lane of column c and
+    // half h holds rows 4h + 0..3 and 8 + 4h + 0..3, which with phi(Q)'s
+    // head dimensions read in the same order (two 8-byte reads) is an
+    // operand as it stands; S enters as the bf16 pair hi + lo.
     {
-      f32x16 acc[2];
+      f32x16 acc[2], den[2];  // numerators; denominator part A 1
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[mb][e] = den[mb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
+        const bf16x8 vt = tr_frag<off256>(L0 + VF, ks * 16, w * 32);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 aa = *(lbf16x8*)(uintptr_t)(L0 + AB + off128(mb * 32 + l32, ks * 16 + hl * 8));
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vb, acc[mb], 0, 0, 0);
+          const bf16x8 at = tr_frag<off128>(L0 + AT, ks * 16, mb * 32);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, at, acc[mb], 0, 0, 0);
+          den[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, at, den[mb], 0, 0, 0);
         }
       }
 #pragma unroll
@@ -264,62 +304,67 @@ __global__ __launch_bounds__(kThreads, 2) void linear_attn_bf16_kernel(LinAttnAr
         const int i = ks >> 1, j0 = (ks & 1) * 2;
         bf16x8 sh, sl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sacc[i][j0 * 4 + e]),
-                                                          __float_as_uint(sacc[i][j0 * 4 + 4 + e]),
-                                                          false, false);
-          const float lo_rows = __uint_as_float(r[0]), hi_rows = __uint_as_float(r[1]);
-          sh[e] = (__bf16)lo_rows;
-          sl[e] = (__bf16)(lo_rows - (float)sh[e]);
-          sh[4 + e] = (__bf16)hi_rows;
-          sl[4 + e] = (__bf16)(hi_rows - (float)sh[4 + e]);
+        for (int e = 0; e < 8; ++e) {
+          const float x = sacc[i][j0 * 4 + e];
+          sh[e] = (__bf16)x;
+          sl[e] = (__bf16)(x - (float)sh[e]);
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 qa = *(lbf16x8*)(uintptr_t)(L0 + QF + off256(mb * 32 + l32, ks * 16 + hl * 8));
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sh, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sl, acc[mb], 0, 0, 0);
+          const int qr = mb * 32 + l32;
+          const bf16x4 q0 = *(const bf16x4*)(lds + QF + off256(qr, ks * 16 + hl * 4));
+          const bf16x4 q1 = *(const bf16x4*)(lds + QF + off256(qr, ks * 16 + 8 + hl * 4));
+          const bf16x8 qb = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, qb, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, qb, acc[mb], 0, 0, 0);
         }
       }
-      const float* den = (const float*)(lds + DN);
-      const int col = w * 32 + l32;
+      const float* dqz = (const float*)(lds + DN);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb) {
+        const int qr = mb * 32 + l32;
+        if (qr < nrows) {
+          // every element of den[mb] in this lane is its query's A 1
+          const float inv = 1.f / (den[mb][0] + dqz[qr]);
+          uint16_t* orow = a.out + ((long)(t0 + qr) * a.Hq + h) * kD + w * 32 + hl * 4;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+          for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = mb * 32 + jj * 8 + hl * 4 + e;
-            if (row < nrows) {
-              const float o = acc[mb][jj * 4 + e] / den[row];
-              *(__bf16*)(a.out + ((long)(t0 + row) * a.Hq + h) * kD + col) = (__bf16)o;
-            }
+            for (int e = 0; e < 4; ++e) v4[e] = (__bf16)(acc[mb][jj * 4 + e] * inv);
+            *(bf16x4*)(orow + jj * 8) = v4;
           }
+        }
+      }
     }
     }  // MODE != 1
 
     // (e) this chunk's phi(K)^T V into S (registers; wave w's columns), and
-    // its keys into z once every wave has read z for the denominators
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 vb = *(lbf16x8*)(uintptr_t)(L0 + VT + off128(w * 32 + l32, ks * 16 + hl * 8));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x8 ka = *(lbf16x8*)(uintptr_t)(L0 + KT + off128(i * 32 + l32, ks * 16 + hl * 8));
-        sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, sacc[i], 0, 0, 0);
-      }
-    }
+    // its key sums phi(K)^T 1 for the 32 head dimensions 32w.. into z (every
+    // wave has read z for the denominators before the last barrier)
     {
-      const int d = tid >> 1, half = tid & 1;
-      float zs = 0.f;
+      f32x16 zacc;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 kv = *(const bf16x8*)(lds + KT + off128(d, half * 32 + j * 8));
+      for (int e = 0; e < 16; ++e) zacc[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zs += (float)kv[e];
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 vb = tr_frag<off256>(L0 + VF, ks * 16, w * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 ka = tr_frag<off256>(L0 + KF, ks * 16, i * 32);
+          sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, vb, sacc[i], 0, 0, 0);
+          if (i == w) zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, ones, zacc, 0, 0, 0);
+        }
       }
-      zs += __shfl_xor(zs, 1, 64);
-      if (half == 0) ((float*)(lds + ZF))[d] += zs;
+      // every column of zacc holds the same sums: lanes 0 and 32 (column 0)
+      // add rows 8jj + 4h + e of block w
+      if (l32 == 0) {
+        float* z = (float*)(lds + ZF) + w * 32 + hl * 4;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[jj * 8 + e] += zacc[jj * 4 + e];
+      }
     }
     __syncthreads();
   }
