@@ -81,7 +81,9 @@ struct Cfg {
   static constexpr int RING_OFF = NBUF * BUF_BYTES;
   static constexpr int RING_BYTES = 2 * BN * 4;
   static constexpr int MISC_OFF = RING_OFF + NRING * RING_BYTES;
-  static constexpr int LDS_BYTES = MISC_OFF + 64;
+  // rotary frequencies (turns per position) of the D/2 pairs, float64
+  static constexpr int ROPE_OFF = MISC_OFF + 64;
+  static constexpr int LDS_BYTES = ROPE_OFF + (D / 2) * 8;
   // copies one wave issues per tile step: two index copies, K and V rows
   static constexpr int COPIES_IDX = 2;
   static constexpr int COPIES_DATA = 2 * WPW;
@@ -263,11 +265,26 @@ __device__ inline void sweep_step_end(int t, int nt) {
 // ----------------------------------------------------------------------------
 // Q fragments with rotary embedding
 // ----------------------------------------------------------------------------
+// x of quad lane k in every lane of the quad (DPP quad_perm(k, k, k, k));
+// k is a constant after unrolling
+__device__ inline float quad_bcast(float x, int k) {
+  const int v = __float_as_int(x);
+  switch (k) {
+    case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false));
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false));
+    default: return __int_as_float(__builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false));
+  }
+}
+
 // Lane l (h = l / 32) holds, for d-step kc, q[row][kc*16 + h*8 + e].
+// Pair j = kc*16 + h*8 + e (kc < KC/2) rotates elements j and j + D/2 by
+// the angle pos * rev[j] turns, reduced to (-1/2, 1/2] in float64 before the
+// hardware sin/cos (which take turns).  `rev` is the frequency table in LDS.
 template <class C>
 __device__ inline void load_q(const AttnArgs& a, long qrow_elem, bool valid, int pos,
-                              bf16x8 (&qf)[C::KC]) {
-  const int h = (threadIdx.x & 63) >> 5;
+                              const double* rev, bf16x8 (&qf)[C::KC]) {
+  const int l = threadIdx.x & 63, h = l >> 5;
   const uint16_t* q = (const uint16_t*)a.q;
   float x[C::KC][8];
 #pragma unroll
@@ -281,24 +298,42 @@ __device__ inline void load_q(const AttnArgs& a, long qrow_elem, bool valid, int
       x[kc][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
   }
+  constexpr int NP = C::KC / 2;  // d-steps of the first half
+  auto rotate = [&](int kc, int e, float s, float c) {
+    const float x1 = x[kc][e], x2 = x[kc + NP][e];
+    x[kc][e] = x1 * c - x2 * s;
+    x[kc + NP][e] = x2 * c + x1 * s;
+  };
   if (a.rope && valid) {
-#pragma unroll
-    for (int kc = 0; kc < C::KC / 2; ++kc) {
+    if ((a.G & 3) == 0) {
+      // G a multiple of 4: the four lanes of a quad hold four heads of one
+      // token (same position, same h), so quad lane k computes the angles
+      // of d-step k (mod NP) once and each d-step's values are broadcast
+      // from its lane (all four lanes share the row's validity)
+      const int k = (l & 3) % NP;
+      float so[8], co[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // the frequency of pair j = kc*16 + h*8 + e, read at indices that
-        // are the same in every lane (scalar loads of the argument) and
-        // selected by h; an index that depends on the lane would make every
-        // lane load its frequencies from memory after its q loads
-        const double rev0 = a.rope_rev[kc * 16 + e], rev1 = a.rope_rev[kc * 16 + 8 + e];
-        double t = (double)pos * (h ? rev1 : rev0);
+        double t = (double)pos * rev[k * 16 + h * 8 + e];
         t -= rint(t);
-        const float s = __builtin_amdgcn_sinf((float)t);
-        const float c = __builtin_amdgcn_cosf((float)t);
-        const float x1 = x[kc][e], x2 = x[kc + C::KC / 2][e];
-        x[kc][e] = x1 * c - x2 * s;
-        x[kc + C::KC / 2][e] = x2 * c + x1 * s;
+        so[e] = __builtin_amdgcn_sinf((float)t);
+        co[e] = __builtin_amdgcn_cosf((float)t);
       }
+#pragma unroll
+      for (int kc = 0; kc < NP; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          rotate(kc, e, quad_bcast(so[e], kc), quad_bcast(co[e], kc));
+        }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < NP; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          double t = (double)pos * rev[kc * 16 + h * 8 + e];
+          t -= rint(t);
+          rotate(kc, e, __builtin_amdgcn_sinf((float)t), __builtin_amdgcn_cosf((float)t));
+        }
     }
   }
 #pragma unroll
@@ -455,7 +490,7 @@ __device__ void attn_item(const AttnArgs& a, int s, int jt, int g, char* lds) {
   const int qpos = rvalid ? a.positions[sg.q0 + i] : -1;
   const long qrow = ((long)(sg.q0 + i) * a.Hq + g * G + hh) * C::D;
   bf16x8 qf[C::KC];
-  load_q<C>(a, qrow, rvalid, qpos, qf);
+  load_q<C>(a, qrow, rvalid, qpos, (const double*)(lds + C::ROPE_OFF), qf);
   const int pos_first = a.positions[sg.q0 + i_first];
   const int pos_last = a.positions[sg.q0 + i_last];
   const int u_end = sg.c + i_last + 1;
@@ -695,6 +730,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
   const int item = blockIdx.x / a.Hkv;
   const int g = blockIdx.x % a.Hkv;
   if (item >= *a.item_count) return;
+  // the rotary frequency table into LDS (read per lane by the query load)
+  if (a.rope && threadIdx.x < D / 2)
+    ((double*)(lds + C::ROPE_OFF))[threadIdx.x] = a.rope_rev[threadIdx.x];
+  __syncthreads();
   const int2 it = a.items[item];
   attn_item<C>(a, it.x, it.y, g, lds);
 }
