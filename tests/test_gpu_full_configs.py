@@ -48,11 +48,13 @@ def _check_segments(wl, call, g, cached_of, score_segs, rng, k_rows=32, full_seg
     H.log(f"{wl.name}: worst error / row-relative bound = {worst:.3f}")
 
 
-def test_gpu_packed_llama8b_full():
+# the workload's own seed and a second one (other lengths and values)
+@pytest.mark.parametrize("seed", [2, 12])
+def test_gpu_packed_llama8b_full(seed):
     import gpu_harness as H
-    wl = W.make("packed_llama8b")
+    wl = W.make("packed_llama8b", seed=seed)
     call = wl.calls[0]
-    H.log(f"packed_llama8b: T={call.T}")
+    H.log(f"packed_llama8b seed {seed}: T={call.T}")
     kc, vc = H.make_caches(wl)
     g = H.gpu_result(H.launch_call(wl, call, kc, vc))
     H.log("packed_llama8b: gpu done, checking")
@@ -120,15 +122,16 @@ def test_gpu_chunked_128k_whole_prompt_full():
     H.log(f"chunked_128k whole prompt: ok ({int(keep.sum())} of 1024 blocks kept)")
 
 
-def test_gpu_mixed_decode_prefill_full():
+@pytest.mark.parametrize("seed", [4, 14])
+def test_gpu_mixed_decode_prefill_full(seed):
     """Decodes over a 17.7 GB cache drawn on the device, plus the prefill
     chunks.  The checked decodes' cached K/V are copied to the host before
     the launch (so the oracle's inputs never pass through the library), and
     after it every cache row outside this call's slots must be unchanged."""
     import gpu_harness as H
-    wl = W.make("mixed_decode_prefill")
+    wl = W.make("mixed_decode_prefill", seed=seed)
     call = wl.calls[0]
-    H.log(f"mixed_decode_prefill: T={call.T} segments={len(call.segments)}")
+    H.log(f"mixed_decode_prefill seed {seed}: T={call.T} segments={len(call.segments)}")
     kc, vc = H.make_caches(wl)
     n_dec = sum(1 for s in call.segments if not s.flagged)
     rng = np.random.default_rng(2)
