@@ -38,8 +38,11 @@ reading is stated in the docstring of the function that makes it.
 
 Parity status: every function here is pinned by tests under ``tests/`` against
 closed forms, a library routine, brute force, or the chunked-prefill example
-printed on the glossary page, except the importance definition itself, which
-no page fixes (parity unpinned beyond the two-formulation agreement check).
+printed on the glossary page.  ``block_mass`` is pinned by its closed form at
+q = 0 (exact rationals) and by a second formulation through block-wise
+log-sum-exps written separately in the tests; what no page fixes is the
+choice of that importance definition, which is a reading (stated at
+``block_mass``), not something a test can pin.
 """
 from __future__ import annotations
 
@@ -189,6 +192,11 @@ def block_mass(q_rot, keys, q_pos, k_pos, n_ctx, n, B, window=0, scale=None, sco
     row t of that block, the exact softmax probabilities over all visible keys
     (cached ones included, so they take part in the normaliser) are summed
     over the own keys of each block.  Cached keys are not scored.
+
+    Reading (the pages name block importance estimated at a full-attention
+    layer, UniPrefill review, "Method & Key Results", but give no formula):
+    the importance of a block is this softmax mass, normalised afterwards by
+    ``normalise_scores``.
 
     scope="prompt" (whole-prompt scoring of a prompt's final chunk): the
     blocks are those of the whole prompt, B keys each from its first key,
