@@ -13,8 +13,9 @@
  *    blocks whose cumulative importance reaches p are kept, and the dropped
  *    tokens skip all later sublayers.
  *  - Ultralytics glossary "Chunked Prefill", "How chunked prefill works": a
- *    chunk attends the cached keys/values of all earlier chunks plus its own
- *    tokens under a causal mask over absolute positions; "Related serving
+ *    prompt fed in pieces gives each piece's queries the keys and values
+ *    stored by the pieces before it together with the piece's own, masked by
+ *    position so that no query sees a later token; "Related serving
  *    techniques": the KV cache lives in fixed-size pages.
  *  - Prepacking summary, "Technical framework" / "Key design": prompts are
  *    concatenated into one sequence with a block-diagonal attention mask and
@@ -145,9 +146,9 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
  * Attention with rotary positions, KV-cache write and fused block mass.
  *
  * Defined by: Ultralytics glossary "Chunked Prefill", "How chunked prefill
- * works" (a chunk attends the cached keys and values of the earlier chunks
- * plus its own tokens, causally over absolute positions, and the result
- * equals one pass) and "Related serving techniques" (KV in fixed-size
+ * works" (a piece of a prompt sees the KV stored by the pieces before it and
+ * its own tokens, masked by position, and the pieces together give the same
+ * result as one pass) and "Related serving techniques" (KV in fixed-size
  * pages); Prepacking summary, "Technical framework" (packed prompts with a
  * block-diagonal mask and positions restarting per prompt); UniPrefill
  * review, "Method & Key Results" (block importance estimated at a
