@@ -12,6 +12,12 @@
 // contiguous in the input and in the output, so each kept block is a
 // contiguous byte range per row tensor; workgroups copy slices of those
 // ranges with 16-byte vector loads and stores and write the index map.
+//
+// Calls with at most kFusedBlocks blocks under segment scope skip pass 1:
+// each copying workgroup sums the kept lengths of the blocks before its own
+// (a few hundred at most, with the block offsets staged in LDS), so one
+// launch does the whole compaction; the launch saved is most of the pass's
+// time at those sizes.
 #include "common.h"
 
 namespace up {
@@ -85,6 +91,8 @@ struct GatherArgs {
   const int32_t* block_out;
   const int32_t* block_seg;
   int32_t* index_map;
+  int32_t* cu_out;    // (one-launch path) per-segment output offsets [S+1]
+  int32_t* num_kept;  // (one-launch path)
   int S, B, n_rows;
   RowCopy rows[kMaxRowTensors];
 };
@@ -165,6 +173,66 @@ __global__ __launch_bounds__(256) void kept_cache_slots_kernel(
   }
 }
 
+// One launch, segment scope, NB <= kFusedBlocks (so S <= kFusedBlocks too):
+// workgroup (k, part) sums (kept ? length : 0) over blocks j < k itself.
+// Every part-0 workgroup writes its segment's output offset when k is the
+// segment's first block, and the one of the last block the kept count.
+constexpr int kFusedBlocks = 512;
+__global__ __launch_bounds__(256) void compact_fused_kernel(GatherArgs g) {
+  __shared__ int32_t cb[kFusedBlocks + 1], cs[kFusedBlocks + 1];
+  __shared__ int32_t wsum[4];
+  const int k = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int S = g.S, B = g.B;
+  for (int i = tid; i <= S; i += 256) {
+    cb[i] = g.cu_blocks[i];
+    cs[i] = g.cu_seqlens[i];
+  }
+  __syncthreads();
+  const int NB = cb[S];
+  if (k >= NB) return;
+  // segment of block j, and its kept own rows (segment scope: blocks start
+  // at the segment's first token)
+  auto seg_of = [&](int j) {
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cb[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  auto kept_len = [&](int j, int sj) {
+    const int i0 = (j - cb[sj]) * B;
+    return g.keep[j] ? min(B, cs[sj + 1] - cs[sj] - i0) : 0;
+  };
+  int part = 0;
+  for (int j = tid; j < k; j += 256) part += kept_len(j, seg_of(j));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+  if (lane == 0) wsum[wid] = part;
+  __syncthreads();
+  const int dst_row = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int s = seg_of(k);
+  const int i0 = (k - cb[s]) * B;
+  const int len = kept_len(k, s);
+  if (blockIdx.y == 0 && tid == 0) {
+    if (k == cb[s]) g.cu_out[s] = dst_row;
+    if (k == NB - 1) {
+      g.cu_out[S] = dst_row + len;
+      *g.num_kept = dst_row + len;
+    }
+  }
+  if (!len) return;
+  const int src_row = cs[s] + i0;
+  const int p = blockIdx.y, nparts = gridDim.y;
+  if (p == 0)
+    for (int r = tid; r < len; r += 256) g.index_map[dst_row + r] = src_row + r;
+  for (int t = 0; t < g.n_rows; ++t) {
+    const long rb = g.rows[t].row_bytes;
+    copy_range(g.rows[t].src + (long)src_row * rb, g.rows[t].dst + (long)dst_row * rb, len * rb,
+               p, nparts);
+  }
+}
+
 hipError_t launch_kept_cache_slots(const int32_t* cu_seqlens, const int32_t* cu_blocks,
                                    const uint8_t* keep, const BlockOrigin& bo,
                                    const int32_t* block_table, int max_pages, int S,
@@ -186,10 +254,14 @@ hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks, c
                           const RowCopy* rows, int n_rows, int32_t* index_map,
                           int32_t* cu_seqlens_out, int32_t* num_kept, int32_t* block_out,
                           int32_t* block_seg, hipStream_t st) {
-  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, cu_blocks, keep,
-                     bo, false, S, block_size, block_out, block_seg, cu_seqlens_out, num_kept);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool fused = !bo.prompt_scope && num_blocks <= kFusedBlocks;
+  if (!fused) {
+    hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, st, cu_seqlens, cu_blocks,
+                       keep, bo, false, S, block_size, block_out, block_seg, cu_seqlens_out,
+                       num_kept);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   GatherArgs g;
   g.cu_seqlens = cu_seqlens;
   g.cu_blocks = cu_blocks;
@@ -198,6 +270,8 @@ hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks, c
   g.block_out = block_out;
   g.block_seg = block_seg;
   g.index_map = index_map;
+  g.cu_out = cu_seqlens_out;
+  g.num_kept = num_kept;
   g.S = S;
   g.B = block_size;
   g.n_rows = n_rows;
@@ -212,7 +286,10 @@ hipError_t launch_compact(const int32_t* cu_seqlens, const int32_t* cu_blocks, c
   int parts = (int)((max_block_bytes + 65535) / 65536);
   if (parts < 1) parts = 1;
   if (parts > 64) parts = 64;
-  hipLaunchKernelGGL(compact_gather_kernel, dim3(num_blocks, parts), dim3(256), 0, st, g);
+  if (fused)
+    hipLaunchKernelGGL(compact_fused_kernel, dim3(num_blocks, parts), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL(compact_gather_kernel, dim3(num_blocks, parts), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 
