@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void kept_cache_slots_kernel(
 // workgroup (k, part) sums (kept ? length : 0) over blocks j < k itself.
 // Every part-0 workgroup writes its segment's output offset when k is the
 // segment's first block, and the one of the last block the kept count.
-constexpr int kFusedBlocks = 512;
+constexpr int kFusedBlocks = 2048;
 __global__ __launch_bounds__(256) void compact_fused_kernel(GatherArgs g) {
   __shared__ int32_t cb[kFusedBlocks + 1], cs[kFusedBlocks + 1];
   __shared__ int32_t wsum[4];
