@@ -97,17 +97,9 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(RopeArgs a) {
   if (slot < 0) return;
   const int page = slot / kPageSize, off = slot % kPageSize;
   const int jg = lane % PG, gl = lane / PG;
+  const int pos = a.rope ? a.positions[t] : 0;
   float c[8], s[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    c[e] = 1.f;
-    s[e] = 0.f;
-  }
-  if (a.rope) {
-    const int pos = a.positions[t];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rope_cs<false>(pos, a.rope_rev[jg * 8 + e], c[e], s[e]);
-  }
+  bool angles = false;
   const uint16_t* k = (const uint16_t*)a.k;
   const uint16_t* v = (const uint16_t*)a.v;
   uint16_t* kc = (uint16_t*)a.k_cache;
@@ -119,6 +111,19 @@ __global__ __launch_bounds__(256) void rope_kv_bf16_kernel(RopeArgs a) {
     const size_t dst = (((size_t)page * a.Hkv + g) * kPageSize + off) * D + jg * 8;
     const u32x4 k1 = *(gcu32x4*)(k + src), k2 = *(gcu32x4*)(k + src + H);
     const u32x4 v1 = *(gcu32x4*)(v + src), v2 = *(gcu32x4*)(v + src + H);
+    // the angles once per token, after the first pass's loads are out, so
+    // their arithmetic runs while the loads are in flight
+    if (!angles) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        c[e] = 1.f;
+        s[e] = 0.f;
+      }
+      if (a.rope)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rope_cs<false>(pos, a.rope_rev[jg * 8 + e], c[e], s[e]);
+      angles = true;
+    }
     u32x4 y1, y2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
