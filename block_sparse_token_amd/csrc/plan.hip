@@ -48,12 +48,30 @@ hipError_t launch_block_offsets(const int32_t* cu_seqlens, const BlockOrigin& bo
   return hipGetLastError();
 }
 
-// One workgroup.  Segments are ranked by the visible-key count of their last
-// row (ctx + n, or the window), heaviest first, ties by index; items are
-// written segment by segment, each segment's tiles from the last (most keys)
-// to the first.  Neighbouring items then read the same segment's keys, so
-// the workgroups that run together on one XCD share its L2, and the longest
-// tiles still start first.  Score items precede all tiles.
+// One workgroup.  Segments fall in two classes: memory-bound ones, whose
+// rows fit in one wave of a tile (8 n <= P: decodes, the tails of short
+// segments), and the rest.  Within its class a segment is ranked by the
+// visible-key count of its last row (ctx + n, or the window), heaviest
+// first, ties by index; its tiles are listed from the last (most keys) to
+// the first, so neighbouring items read the same segment's keys and the
+// workgroups that run together on one XCD share its L2.  The two class
+// lists are then merged in proportion (item i of a class of N items sits at
+// fraction (2i + 1) / 2N, memory-bound first on ties), so that workgroups
+// streaming cached keys run beside workgroups bound by the matrix cores,
+// and the lightest items of both end the list.  Score items precede all
+// tiles.
+__device__ inline bool memory_bound_segment(int n, int P) { return 8 * n <= P; }
+
+// Items of the other class (Y, NY items) ahead of item i of class X (NX
+// items): #{j : (2j + 1) NX < (2i + 1) NY}, or <= when ties go to X's side
+// of the merge.
+__device__ inline int merged_before(int i, long NX, long NY, bool ties_ahead) {
+  if (NY == 0) return 0;
+  const long A = (2L * i + 1) * NY;
+  const long c = ties_ahead ? (A / NX + 1) / 2 : ((A + NX - 1) / NX) / 2;
+  return (int)min(c, NY);
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu_seqlens,
                                                     const int32_t* __restrict__ ctx_lens,
                                                     const uint8_t* __restrict__ score_flags,
@@ -61,35 +79,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int2* __restrict__ items,
                                                     int32_t* __restrict__ count, int capacity) {
   __shared__ int32_t key[kMaxSeqsPlan];
-  __shared__ int32_t order[kMaxSeqsPlan];
+  __shared__ int32_t order[kMaxSeqsPlan];  // memory-bound class first, each by rank
   __shared__ int32_t cu_t[kMaxSeqsPlan + 1];
   __shared__ int32_t wsum[16];
-  __shared__ int32_t carry, n_score;
+  __shared__ int32_t carry, n_score, n_mem;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (tid == 0) {
     carry = 0;
     n_score = 0;
+    n_mem = 0;
     cu_t[0] = 0;
   }
+  __syncthreads();
   for (int s = tid; s < S; s += 1024) {
     const int n = cu_seqlens[s + 1] - cu_seqlens[s];
     int k = ctx_lens[s] + n;
     if (window > 0) k = min(k, window + P);
-    key[s] = k;
+    // the class rides in the key's sign bit: memory-bound keys are negative
+    key[s] = memory_bound_segment(n, P) ? -1 - k : k;
+    if (memory_bound_segment(n, P)) atomicAdd(&n_mem, 1);
   }
   __syncthreads();
+  const int S_mem = n_mem;
   for (int s = tid; s < S; s += 1024) {
     const int ks = key[s];
+    const bool mem = ks < 0;
     int r = 0;
     for (int t = 0; t < S; ++t) {
       const int kt = key[t];
-      r += (kt > ks) || (kt == ks && t < s);
+      if ((kt < 0) != mem) continue;
+      // heaviest first: for negative keys -1 - k, the smaller key is heavier
+      const bool heavier = mem ? kt < ks : kt > ks;
+      r += heavier || (kt == ks && t < s);
     }
-    order[r] = s;
+    order[(mem ? 0 : S_mem) + r] = s;
     if (score_flags && score_flags[s]) atomicAdd(&n_score, 1);
   }
   __syncthreads();
-  // tiles per segment in rank order, prefix-summed
+  // tiles per segment in class-then-rank order, prefix-summed
   for (int base = 0; base < S; base += 1024) {
     const int r = base + tid;
     int v = 0;
@@ -113,6 +140,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
   }
   const int n_tiles = cu_t[S];
+  const int n_mem_tiles = cu_t[S_mem];
   const int ns = n_score;
   if (tid == 0) {
     int k = 0;
@@ -121,8 +149,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         if (score_flags[order[r]]) items[k++] = make_int2(order[r], kScoreTile);
     *count = min(n_tiles + ns, capacity);
   }
+  const long NM = n_mem_tiles, NC = n_tiles - n_mem_tiles;
   for (int i = tid; i < n_tiles; i += 1024) {
-    int lo = 0, hi = S - 1;  // rank r with cu_t[r] <= i < cu_t[r+1]
+    int lo = 0, hi = S - 1;  // position r with cu_t[r] <= i < cu_t[r+1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (cu_t[mid] <= i) lo = mid; else hi = mid - 1;
@@ -130,7 +159,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     const int s = order[lo];
     const int nt = cu_t[lo + 1] - cu_t[lo];
     const int j = nt - 1 - (i - cu_t[lo]);
-    if (ns + i < capacity) items[ns + i] = make_int2(s, j);
+    const bool mem = i < n_mem_tiles;
+    const int ic = mem ? i : i - n_mem_tiles;
+    const int pos = ic + (mem ? merged_before(ic, NM, NC, false) : merged_before(ic, NC, NM, true));
+    if (ns + pos < capacity) items[ns + pos] = make_int2(s, j);
   }
 }
 
