@@ -327,8 +327,7 @@ up_status prefill_attn_impl(const up_batch* batch, up_dtype dtype, int32_t Hq, i
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
     return fail(UP_ERR_INVALID, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
   const int G = Hq / Hkv;
-  if (G > 32 || (G & (G - 1)))
-    return fail(UP_ERR_UNSUPPORTED, "Hq / Hkv must be a power of two <= 32 (got %d)", G);
+  if (G > 32) return fail(UP_ERR_UNSUPPORTED, "Hq / Hkv must be at most 32 (got %d)", G);
   if (Hkv > 255) return fail(UP_ERR_UNSUPPORTED, "at most 255 KV heads (got %d)", Hkv);
   if (D != 64 && D != 128) return fail(UP_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %d)", D);
   if (!q || !k || !v || !k_cache || !v_cache || !out)

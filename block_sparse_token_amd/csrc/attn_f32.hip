@@ -170,7 +170,10 @@ __device__ void score_item_f(const AttnArgs& a, int s, int g, char* lds) {
   const int nb = (sg.n + B - 1) / B;
   const int r0 = (nb - 1) * B;
   const int rows_total = (sg.n - r0) * G;
-  const int passes = (rows_total + NT - 1) / NT;
+  // a pass covers whole tokens (NTG rows, a multiple of G), so thread t
+  // holds head t % G in every pass
+  const int NTG = (NT / G) * G;
+  const int passes = (rows_total + NTG - 1) / NTG;
   const long mbase = a.cu_blocks[s];
   const float* sK = (const float*)(lds + CfgF<D>::K_OFF);
   const int* sP = (const int*)(lds + CfgF<D>::POS_OFF);
@@ -178,7 +181,7 @@ __device__ void score_item_f(const AttnArgs& a, int s, int g, char* lds) {
   // a tile of BN = 32 own keys aligned to the segment start meets at most
   // two blocks (block sizes are multiples of 16)
   for (int ps = passes - 1; ps >= 0; --ps) {
-    const int rbeg = ps * NT, rend = min(rows_total, rbeg + NT);
+    const int rbeg = ps * NTG, rend = min(rows_total, rbeg + NTG);
     const int r = rbeg + threadIdx.x;
     const bool valid = r < rend;
     const int i = r0 + r / G, hh = r % G;

@@ -180,8 +180,9 @@ size_t up_attn_workspace_bytes(const up_batch* batch, up_dtype dtype, int32_t Hq
  *
  * dtype: UP_F32 (q, k, v, caches, out float32) or UP_BF16 (all bf16;
  *        products on bf16 matrix cores, softmax and accumulation in fp32).
- * Hq % Hkv == 0 (else UP_ERR_INVALID).  Built: Hq / Hkv a power of two
- * <= 32, Hkv <= 255, D in {64, 128}, at most 4096 segments per call
+ * Hq % Hkv == 0 (else UP_ERR_INVALID).  Built: Hq / Hkv <= 32 (any
+ * group size: 4 for Llama-3, 7 for 28 query over 4 KV heads), Hkv <= 255,
+ * D in {64, 128}, at most 4096 segments per call
  * (num_seqs); other values return UP_ERR_UNSUPPORTED.
  * q [T, Hq, D], k, v [T, Hkv, D] row-major, read-only.
  * k_cache, v_cache [num_pages, Hkv, page_size, D], read and written.

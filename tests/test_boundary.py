@@ -66,7 +66,7 @@ def test_attention_argument_validation(L):
     b = _batch()
     assert _attn(L, None) == UP_ERR_INVALID
     assert _attn(L, b, Hq=6, Hkv=4) == UP_ERR_INVALID
-    assert _attn(L, b, Hq=12, Hkv=4) == UP_ERR_UNSUPPORTED  # G = 3
+    assert _attn(L, b, Hq=66, Hkv=2) == UP_ERR_UNSUPPORTED  # G = 33
     assert _attn(L, b, Hq=256, Hkv=256) == UP_ERR_UNSUPPORTED  # cache rows use 24-bit products
     assert _attn(L, b, D=96) == UP_ERR_UNSUPPORTED
     assert _attn(L, b, dtype=7) == UP_ERR_UNSUPPORTED

@@ -99,6 +99,22 @@ CASES = [
     dict(lengths=[400, 70], ctxs=[16, 0], Hq=4, Hkv=2, D=64, dtype="f32", block_size=48,
          p=0.5, theta=500000.0, window=90),
     dict(lengths=[600], ctxs=[0], Hq=2, Hkv=2, D=128, dtype="f32", block_size=256, p=0.9),
+    # query groups that are not powers of two: a tile holds 256 // G
+    # positions (bf16) or 128 // G (fp32) and leaves the remaining rows
+    # unused; G = 12 takes the per-quad rotary path, the others the per-lane
+    # one; the fp32 scoring passes cover whole tokens (126 rows at G = 6)
+    dict(lengths=[700, 1, 130], ctxs=[0, 500, 70], Hq=12, Hkv=4, D=128, dtype="bf16",
+         block_size=64, p=0.9, theta=500000.0),
+    dict(lengths=[333, 90], ctxs=[64, 0], Hq=40, Hkv=8, D=128, dtype="bf16", block_size=32,
+         p=0.8, theta=500000.0, window=150),
+    dict(lengths=[500, 47], ctxs=[0, 200], Hq=28, Hkv=4, D=64, dtype="bf16", block_size=16,
+         p=0.95, theta=1000000.0),
+    dict(lengths=[400, 5], ctxs=[0, 100], Hq=24, Hkv=2, D=128, dtype="bf16", block_size=64,
+         p=0.9, theta=500000.0),
+    dict(lengths=[300, 45], ctxs=[0, 20], Hq=12, Hkv=2, D=64, dtype="f32", block_size=64,
+         p=0.9, theta=10000.0),
+    dict(lengths=[200], ctxs=[30], Hq=6, Hkv=2, D=128, dtype="f32", block_size=32, p=0.8,
+         theta=500000.0, window=60),
 ]
 
 
