@@ -61,15 +61,20 @@ hipError_t launch_block_offsets(const int32_t* cu_seqlens, const BlockOrigin& bo
 // and the lightest items of both end the list.  Score items precede all
 // tiles.
 __device__ inline bool memory_bound_segment(int n, int P) { return 8 * n <= P; }
+constexpr int kClassBit = 1 << 30;
 
 // Items of the other class (Y, NY items) ahead of item i of class X (NX
 // items): #{j : (2j + 1) NX < (2i + 1) NY}, or <= when ties go to X's side
 // of the merge.
-__device__ inline int merged_before(int i, long NX, long NY, bool ties_ahead) {
+// The quotient runs in double: A and NX are integers below 2^53, and the
+// quotient of two such integers is at least 1/NX away from any integer it
+// does not equal, far more than its rounding error, so floor and ceil are
+// exact.
+__device__ inline int merged_before(int i, int NX, int NY, bool ties_ahead) {
   if (NY == 0) return 0;
-  const long A = (2L * i + 1) * NY;
-  const long c = ties_ahead ? (A / NX + 1) / 2 : ((A + NX - 1) / NX) / 2;
-  return (int)min(c, NY);
+  const double q = ((2.0 * i + 1.0) * NY) / NX;
+  const int c = ties_ahead ? ((int)floor(q) + 1) / 2 : (int)ceil(q) / 2;
+  return min(c, NY);
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu_seqlens,
@@ -91,26 +96,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     cu_t[0] = 0;
   }
   __syncthreads();
-  for (int s = tid; s < S; s += 1024) {
-    const int n = cu_seqlens[s + 1] - cu_seqlens[s];
-    int k = ctx_lens[s] + n;
-    if (window > 0) k = min(k, window + P);
-    // the class rides in the key's sign bit: memory-bound keys are negative
-    key[s] = memory_bound_segment(n, P) ? -1 - k : k;
-    if (memory_bound_segment(n, P)) atomicAdd(&n_mem, 1);
+  for (int base = 0; base < S; base += 1024) {
+    const int s = base + tid;
+    bool mem = false;
+    if (s < S) {
+      const int n = cu_seqlens[s + 1] - cu_seqlens[s];
+      int k = ctx_lens[s] + n;
+      if (window > 0) k = min(k, window + P);
+      // the class rides in bit 30 of the key (key counts clamped below it)
+      mem = memory_bound_segment(n, P);
+      key[s] = min(k, kClassBit - 1) | (mem ? kClassBit : 0);
+    }
+    const unsigned long long m = __ballot(mem);
+    if (lane == 0 && m) atomicAdd(&n_mem, __popcll(m));
   }
   __syncthreads();
   const int S_mem = n_mem;
   for (int s = tid; s < S; s += 1024) {
     const int ks = key[s];
-    const bool mem = ks < 0;
+    const bool mem = (ks & kClassBit) != 0;
     int r = 0;
     for (int t = 0; t < S; ++t) {
       const int kt = key[t];
-      if ((kt < 0) != mem) continue;
-      // heaviest first: for negative keys -1 - k, the smaller key is heavier
-      const bool heavier = mem ? kt < ks : kt > ks;
-      r += heavier || (kt == ks && t < s);
+      // same class, heavier (or as heavy and earlier)
+      r += (((kt ^ ks) & kClassBit) == 0) & ((kt > ks) | ((kt == ks) & (t < s)));
     }
     order[(mem ? 0 : S_mem) + r] = s;
     if (score_flags && score_flags[s]) atomicAdd(&n_score, 1);
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         if (score_flags[order[r]]) items[k++] = make_int2(order[r], kScoreTile);
     *count = min(n_tiles + ns, capacity);
   }
-  const long NM = n_mem_tiles, NC = n_tiles - n_mem_tiles;
+  const int NM = n_mem_tiles, NC = n_tiles - n_mem_tiles;
   for (int i = tid; i < n_tiles; i += 1024) {
     int lo = 0, hi = S - 1;  // position r with cu_t[r] <= i < cu_t[r+1]
     while (lo < hi) {
