@@ -64,12 +64,12 @@ __device__ inline bool memory_bound_segment(int n, int P) { return 8 * n <= P; }
 constexpr int kClassBit = 1 << 30;
 
 // Items of the other class (Y, NY items) ahead of item i of class X (NX
-// items): #{j : (2j + 1) NX < (2i + 1) NY}, or <= when ties go to X's side
-// of the merge.
-// The quotient runs in double: A and NX are integers below 2^53, and the
-// quotient of two such integers is at least 1/NX away from any integer it
-// does not equal, far more than its rounding error, so floor and ceil are
-// exact.
+// items): #{j : (2j + 1) NX < (2i + 1) NY}, with <= instead of < when a
+// Y item at the same fraction goes first (ties_ahead: X is the
+// compute-bound class).  The quotient runs in double: numerator and NX are
+// integers below 2^53, and their quotient is at least 1/NX away from any
+// integer it does not equal, far more than its rounding error, so floor
+// and ceil are exact.
 __device__ inline int merged_before(int i, int NX, int NY, bool ties_ahead) {
   if (NY == 0) return 0;
   const double q = ((2.0 * i + 1.0) * NY) / NX;
