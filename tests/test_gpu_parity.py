@@ -115,6 +115,9 @@ CASES = [
          p=0.9, theta=10000.0),
     dict(lengths=[200], ctxs=[30], Hq=6, Hkv=2, D=128, dtype="f32", block_size=32, p=0.8,
          theta=500000.0, window=60),
+    # D = 64 at G = 6 (42 positions per tile) with decodes and a window
+    dict(lengths=[1, 250, 1, 90], ctxs=[700, 0, 45, 33], flags=[False, True, False, True],
+         Hq=12, Hkv=2, D=64, dtype="bf16", block_size=32, p=0.9, theta=500000.0, window=120),
 ]
 
 
@@ -174,13 +177,24 @@ def test_gpu_whole_prompt_scoring(B, lengths, ctxs, flags, p):
     """Final chunks scored over their whole prompt (cached blocks included):
     block scores, selection and compaction by prompt block, and the KV slots
     of the kept cached tokens, against the oracle."""
+    _whole_prompt_case(B, lengths, ctxs, flags, p)
+
+
+def test_gpu_whole_prompt_scoring_query_group_of_five():
+    """The same with 20 query heads over 4 KV heads (a tile of 51 positions,
+    one packed row unused) and a decode segment beside the scored ones."""
+    _whole_prompt_case(64, [150, 1, 70], [256, 300, 128], [True, False, True], 0.7, Hq=20, Hkv=4,
+                       seed=7105)
+
+
+def _whole_prompt_case(B, lengths, ctxs, flags, p, Hq=8, Hkv=2, seed=None):
     import torch
     import gpu_harness as H
     from block_sparse_token_amd import binding as Bd
 
-    wl = W.custom(seed=7000 + B, hidden_width=64, lengths=lengths, ctxs=ctxs, flags=flags, Hq=8,
-                  Hkv=2, D=128, dtype="bf16", block_size=B, p=p, theta=500000.0,
-                  scale=1.0 / np.sqrt(128.0))
+    wl = W.custom(seed=7000 + B if seed is None else seed, hidden_width=64, lengths=lengths,
+                  ctxs=ctxs, flags=flags, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16", block_size=B, p=p,
+                  theta=500000.0, scale=1.0 / np.sqrt(128.0))
     call = wl.calls[0]
     H.log(f"whole-prompt scoring B={B} lens={lengths} ctx={ctxs} flags={flags} p={p}")
     ref = driver.run_workload(wl, layer2=False, scope="prompt")[0]
