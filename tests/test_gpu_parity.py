@@ -118,6 +118,9 @@ CASES = [
     # D = 64 at G = 6 (42 positions per tile) with decodes and a window
     dict(lengths=[1, 250, 1, 90], ctxs=[700, 0, 45, 33], flags=[False, True, False, True],
          Hq=12, Hkv=2, D=64, dtype="bf16", block_size=32, p=0.9, theta=500000.0, window=120),
+    # the largest KV head count the cache addressing accepts (255, G = 1)
+    dict(lengths=[40, 17], ctxs=[20, 0], Hq=255, Hkv=255, D=64, dtype="bf16", block_size=16,
+         p=0.9, theta=500000.0),
 ]
 
 
