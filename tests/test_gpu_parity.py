@@ -121,6 +121,12 @@ CASES = [
     # the largest KV head count the cache addressing accepts (255, G = 1)
     dict(lengths=[40, 17], ctxs=[20, 0], Hq=255, Hkv=255, D=64, dtype="bf16", block_size=16,
          p=0.9, theta=500000.0),
+    # degenerate windows: one key (each token sees itself only) and one wider
+    # than every distance (full causal), with cached prefixes
+    dict(lengths=[130, 64, 1], ctxs=[0, 40, 90], Hq=8, Hkv=2, D=128, dtype="bf16", block_size=64,
+         p=0.9, theta=500000.0, window=1),
+    dict(lengths=[300, 77], ctxs=[50, 0], Hq=8, Hkv=2, D=128, dtype="bf16", block_size=64,
+         p=0.9, theta=500000.0, window=1 << 20),
 ]
 
 
